@@ -1,0 +1,223 @@
+"""Python binding of the CPU oracle (``headq_oracle.c``) — TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check and the CPU-baseline leg of the benchmark may import this
+module. The product library never imports it and shares no code with it.
+
+What it computes is cited in ``headq_oracle.c`` (HeadQ technical summary, §3 steps 1-3; §1 and
+§2.2 for the readout). This file only marshals numpy arrays into the C calls and assembles the
+per-stream results into the cache format.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from pathlib import Path
+
+import numpy as np
+
+_HERE = Path(__file__).resolve().parent
+_SRC = _HERE / "headq_oracle.c"
+_LIB = _HERE / "liboracle.so"
+GROUP = 32
+
+_CFLAGS = ["-O2", "-std=c11", "-Wall", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
+
+
+def build(force: bool = False) -> Path:
+    """Compile the oracle with gcc (no contraction, IEEE semantics)."""
+    if force or not _LIB.exists() or _LIB.stat().st_mtime < _SRC.stat().st_mtime:
+        tmp = _LIB.with_suffix(f".so.tmp{os.getpid()}")
+        subprocess.run(["gcc", *_CFLAGS, str(_SRC), "-o", str(tmp), "-lm"], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build()
+        L = ctypes.CDLL(str(_LIB))
+        P, I, I64, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
+        L.orc_f32_to_f16.restype = ctypes.c_uint16
+        L.orc_f32_to_f16.argtypes = [ctypes.c_float]
+        L.orc_f16_to_f32.restype = ctypes.c_float
+        L.orc_f16_to_f32.argtypes = [ctypes.c_uint16]
+        for name in ("orc_f32_to_f16_array", "orc_f16_to_f32_array", "orc_f32_to_bf16_array"):
+            getattr(L, name).argtypes = [P, P, I64]
+            getattr(L, name).restype = None
+        L.orc_calibrate.argtypes = [I, I, I, I64, I, I, P, P, P]
+        L.orc_encode_keys.argtypes = [I, I, I, I, I64, P, P, P, P, P, P, P, P, P]
+        L.orc_quantize_values.argtypes = [I, I, I64, P, P, P, P]
+        L.orc_pack_kcode.argtypes = [I, I64, P, P]
+        L.orc_pack_kmeta.argtypes = [I, I64, P, P, P]
+        L.orc_pack_scode.argtypes = [I, I64, P, P]
+        L.orc_pack_vdense.argtypes = [I, I64, I, P, P]
+        L.orc_pack_vcode.argtypes = [I, I64, P, P]
+        L.orc_pack_vmeta.argtypes = [I, I64, P, P, P]
+        L.orc_decode.argtypes = [I, I, I, I, I, I, I, I64, I64, P, P, P, P, P, P, P, P, P, D, I, I, P, P]
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return None if a is None else ctypes.c_void_p(a.ctypes.data)
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError(f"oracle {what} rejected its arguments (rc={rc})")
+
+
+# --------------------------------------------------------------------------------------------
+# number formats
+
+def f32_to_f16_bits(x) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint16)
+    lib().orc_f32_to_f16_array(_p(x), _p(out), x.size)
+    return out
+
+
+def f16_bits_to_f32(h) -> np.ndarray:
+    h = np.ascontiguousarray(h, dtype=np.uint16)
+    out = np.empty(h.shape, dtype=np.float32)
+    lib().orc_f16_to_f32_array(_p(h), _p(out), h.size)
+    return out
+
+
+def f32_to_bf16_bits(x) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint16)
+    lib().orc_f32_to_bf16_array(_p(x), _p(out), x.size)
+    return out
+
+
+def bf16_bits_to_f32(h) -> np.ndarray:
+    h = np.ascontiguousarray(h, dtype=np.uint16)
+    return (h.astype(np.uint32) << 16).view(np.float32)
+
+
+# --------------------------------------------------------------------------------------------
+# calibration, encode, decode
+
+def calibrate(q_cal, n_kv_heads: int, rank: int, centered: bool = False):
+    """Per-KV-head query PCA. q_cal: f32 [Hq][n_cal][d] -> (U f32 [Hkv][d][r], eig f64 [Hkv][r])."""
+    q = np.ascontiguousarray(q_cal, dtype=np.float32)
+    hq, n_cal, d = q.shape
+    U = np.zeros((n_kv_heads, d, rank), dtype=np.float32)
+    eig = np.zeros((n_kv_heads, rank), dtype=np.float64)
+    _check(lib().orc_calibrate(d, hq, n_kv_heads, n_cal, rank, int(centered), _p(q), _p(U), _p(eig)),
+           "calibrate")
+    return U, eig
+
+
+def encode_keys(k, U, bits: int = 2, side_bits: int = 4):
+    """Encode one key stream. k: f32 [T][d], U: f32 [d][r] (or None for r = 0)."""
+    k = np.ascontiguousarray(k, dtype=np.float32)
+    T, d = k.shape
+    r = 0 if U is None else U.shape[1]
+    Uc = None if U is None else np.ascontiguousarray(U, dtype=np.float32)
+    out = dict(
+        codes=np.zeros((T, d), np.uint8), scale=np.zeros((T // GROUP, d), np.uint16),
+        zero=np.zeros((T // GROUP, d), np.uint16), zc=np.zeros((T, max(r, 1)), np.int8)[:, :r].copy(),
+        sigma=np.zeros(T, np.uint16), resid=np.zeros((T, d), np.float32), proj=np.zeros((T, max(r, 1)), np.float32),
+    )
+    zc_buf = out["zc"] if r else None
+    _check(lib().orc_encode_keys(d, r, bits, side_bits, T, _p(k), _p(Uc), _p(out["codes"]), _p(out["scale"]),
+                                 _p(out["zero"]), _p(zc_buf), _p(out["sigma"]), _p(out["resid"]), _p(out["proj"])),
+           "encode_keys")
+    out["proj"] = out["proj"][:, :r]
+    return out
+
+
+def quantize_values(v, bits: int = 2):
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    T, d = v.shape
+    codes = np.zeros((T, d), np.uint8)
+    scale = np.zeros((T, d // GROUP), np.uint16)
+    zero = np.zeros((T, d // GROUP), np.uint16)
+    _check(lib().orc_quantize_values(d, bits, T, _p(v), _p(codes), _p(scale), _p(zero)), "quantize_values")
+    return dict(codes=codes, scale=scale, zero=zero)
+
+
+def empty_cache(B, Hkv, cap, d, r, value_mode, value_dtype):
+    """Zero-filled buffers of the cache format (numpy, host)."""
+    c = dict(
+        kcode=np.zeros((B, Hkv, cap, d // 4), np.uint8),
+        kmeta=np.zeros((B, Hkv, cap // GROUP, 2, d), np.uint16),
+        scode=np.zeros((B, Hkv, cap, max(r // 2, 0)), np.uint8),
+        ssc=np.zeros((B, Hkv, cap), np.uint16),
+    )
+    if value_mode == 0:
+        dt = np.float32 if value_dtype == 0 else np.uint16
+        c["v"] = np.zeros((B, Hkv, cap // GROUP, d, GROUP), dt)
+    else:
+        c["vcode"] = np.zeros((B, Hkv, cap // GROUP, d, 8), np.uint8)
+        c["vmeta"] = np.zeros((B, Hkv, cap // GROUP, 2, d // GROUP, GROUP), np.uint16)
+    return c
+
+
+def write_stream(cache, b, h, start, k, v, U_h, value_mode, value_dtype, bits=2, side_bits=4):
+    """Encode keys (and values) of one (b, h) stream into `cache` at token offset `start`.
+
+    k: f32 [n][d] keys (exact widening of the stored key dtype)
+    v: [n][d] values (f32 array for dtype 0, bf16 bit patterns uint16 for dtype 1, f32 for 2-bit)
+    Returns the unpacked encode result for inspection."""
+    n, d = k.shape
+    r = 0 if U_h is None else U_h.shape[1]
+    enc = encode_keys(k, U_h, bits, side_bits)
+    L = lib()
+    g0, g1 = start // GROUP, (start + n) // GROUP
+    kc = np.zeros((n, d // 4), np.uint8)
+    _check(L.orc_pack_kcode(d, n, _p(enc["codes"]), _p(kc)), "pack_kcode")
+    cache["kcode"][b, h, start:start + n] = kc
+    km = np.zeros((n // GROUP, 2, d), np.uint16)
+    _check(L.orc_pack_kmeta(d, n, _p(enc["scale"]), _p(enc["zero"]), _p(km)), "pack_kmeta")
+    cache["kmeta"][b, h, g0:g1] = km
+    if r:
+        sc = np.zeros((n, r // 2), np.uint8)
+        _check(L.orc_pack_scode(r, n, _p(np.ascontiguousarray(enc["zc"])), _p(sc)), "pack_scode")
+        cache["scode"][b, h, start:start + n] = sc
+    cache["ssc"][b, h, start:start + n] = enc["sigma"]
+    if v is not None:
+        if value_mode == 0:
+            src = np.ascontiguousarray(v)
+            eb = src.dtype.itemsize
+            dst = np.zeros((n // GROUP, d, GROUP), src.dtype)
+            _check(L.orc_pack_vdense(d, n, eb, _p(src), _p(dst)), "pack_vdense")
+            cache["v"][b, h, g0:g1] = dst
+        else:
+            vq = quantize_values(v, bits)
+            vc = np.zeros((n // GROUP, d, 8), np.uint8)
+            _check(L.orc_pack_vcode(d, n, _p(vq["codes"]), _p(vc)), "pack_vcode")
+            cache["vcode"][b, h, g0:g1] = vc
+            vm = np.zeros((n // GROUP, 2, d // GROUP, GROUP), np.uint16)
+            _check(L.orc_pack_vmeta(d, n, _p(vq["scale"]), _p(vq["zero"]), _p(vm)), "pack_vmeta")
+            cache["vmeta"][b, h, g0:g1] = vm
+    return enc
+
+
+def decode(cache, q, U, n_ctx, kappa=1.0, value_mode=0, value_dtype=1, b_range=None, want_logits=True):
+    """fp64 decode attention from the packed cache.
+
+    q: f32 [B][Hq][d]; U: f32 [Hkv][d][r] (or None). Returns (logits f64 [B][Hq][n_ctx] natural-log
+    units or None, out f64 [B][Hq][d]); rows outside b_range stay zero."""
+    kcode = np.ascontiguousarray(cache["kcode"])
+    B, Hkv, cap, _ = kcode.shape
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    _, Hq, d = q.shape
+    r = 0 if U is None else U.shape[2]
+    b0, b1 = (0, B) if b_range is None else b_range
+    out = np.zeros((B, Hq, d), np.float64)
+    logits = np.zeros((B, Hq, n_ctx), np.float64) if want_logits else None
+    arrs = {k: np.ascontiguousarray(val) for k, val in cache.items()}
+    Uc = None if U is None else np.ascontiguousarray(U, dtype=np.float32)
+    _check(lib().orc_decode(d, Hq, Hkv, r, value_mode, value_dtype, B, cap, n_ctx, _p(arrs["kcode"]),
+                            _p(arrs["kmeta"]), _p(arrs["scode"]) if r else None, _p(arrs["ssc"]) if r else None,
+                            _p(arrs.get("v")), _p(arrs.get("vcode")), _p(arrs.get("vmeta")), _p(Uc), _p(q),
+                            float(kappa), b0, b1, _p(logits), _p(out)), "decode")
+    return logits, out
