@@ -1,0 +1,197 @@
+/*
+ * headq.h — C ABI of libheadq, the HeadQ key-side KV-cache hot path for AMD Instinct MI355X
+ * (gfx950, CDNA4).
+ *
+ * HeadQ ("HeadQ: Model-Visible Distortion and Score-Space Correction for KV-Cache
+ * Quantization"; Dutch technical summary "Technische Samenvatting", §3 "Algorithmisch
+ * Overzicht") keeps each cached key as a low-bit base code plus a low-rank side code of its
+ * residual in a query basis U_h, and adds the side code back as a logit correction at decode:
+ *
+ *   calibrate  U_h = top-r principal directions of post-RoPE calibration queries   (§3 step 1)
+ *   write      k_base = B_b(k);  e = k - k_base;  z = Q_q(U_h^T e)                  (§3 step 2)
+ *   read       s_j = q.k_base_j / sqrt(d) + (U_h^T q).z_hat_j / sqrt(d), softmax, sum_j p_j v_j
+ *                                                                                   (§3 step 3)
+ *
+ * Three calls, one per phase: headq_calibrate (host), headq_cache_append (GPU),
+ * headq_decode_attn (GPU).
+ *
+ * Conventions
+ *   Ownership  The caller owns every buffer. The library never allocates, frees or keeps device
+ *              memory and holds no mutable global state; calls are re-entrant.
+ *   Streams    GPU calls enqueue work on `stream` (a hipStream_t; NULL = the null stream) and
+ *              return without synchronizing. Set HEADQ_SYNC_DEBUG=1 in the environment to make
+ *              each GPU call synchronize and report asynchronous errors.
+ *   Errors     Every argument is checked on the host before any HIP call, so a rejected call
+ *              enqueues nothing. HEADQ_ERR_HIP reports a launch (or, in debug mode, execution)
+ *              error from the HIP runtime.
+ *   Numbers    fp16 = IEEE binary16 bits (uint16_t); bf16 = bfloat16 bits (uint16_t); both
+ *              rounded to nearest even wherever the library produces them.
+ *   Preconditions not checked on the device: keys, values and queries are finite and below
+ *              65504 in magnitude (binary16 metadata must not overflow).
+ *
+ * Cache format (per layer). Every buffer is indexed [b][h] first (batch, KV head), then by
+ * token; `cap` = capacity in tokens (a multiple of 32); G = 32 tokens per group; d = head_dim;
+ * r = rank. All buffers must be 16-byte aligned.
+ *   kcode  u8   [B][Hkv][cap][d/4]       2-bit base codes; byte c/4 holds channel c at bits 2(c%4)
+ *   kmeta  fp16 [B][Hkv][cap/G][2][d]    per (group, channel): row 0 = step s, row 1 = zero z
+ *   scode  u8   [B][Hkv][cap][r/2]       4-bit side codes u = zc + 8; component 2i in the low
+ *                                        nibble of byte i, component 2i+1 in the high nibble
+ *   ssc    fp16 [B][Hkv][cap]            per-token side step sigma (z_hat = sigma * zc)
+ *   v      (dense values) f32 or bf16 [B][Hkv][cap/G][d][G]: within a 32-token group the values
+ *                                        are stored channel-major (token index fastest)
+ *   vcode  u8   [B][Hkv][cap/G][d][8]    (2-bit values) channel c, group token t = 4b+m at
+ *                                        byte b, bits 2m
+ *   vmeta  fp16 [B][Hkv][cap/G][2][d/32][G]  (2-bit values) per (token, 32-channel group):
+ *                                        row 0 = step, row 1 = zero, token index fastest
+ *   U      f32  [Hkv][d][r]              the side basis (device copy of headq_calibrate's output)
+ */
+#ifndef HEADQ_H
+#define HEADQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum headq_status {
+  HEADQ_OK = 0,
+  HEADQ_ERR_NULL = 1,        /* a required pointer is NULL */
+  HEADQ_ERR_SHAPE = 2,       /* inconsistent or out-of-range dimensions */
+  HEADQ_ERR_ALIGN = 3,       /* a token count/offset is not a multiple of 32, or a buffer or
+                                stride breaks the 16-byte alignment rule */
+  HEADQ_ERR_CAPACITY = 4,    /* start + n_new > capacity, or n_ctx > capacity */
+  HEADQ_ERR_WORKSPACE = 5,   /* *ws_bytes smaller than the size this call needs */
+  HEADQ_ERR_NUMERIC = 6,     /* non-finite calibration input */
+  HEADQ_ERR_UNSUPPORTED = 7, /* a well-formed setting this build does not implement */
+  HEADQ_ERR_HIP = 8          /* the HIP runtime reported an error */
+} headq_status;
+
+/* element types */
+enum { HEADQ_F32 = 0, HEADQ_BF16 = 1 };
+/* value storage */
+enum { HEADQ_V_DENSE = 0, HEADQ_V_Q2 = 1 };
+
+typedef struct headq_config {
+  int32_t head_dim;    /* d: 64 or 128 */
+  int32_t n_q_heads;   /* Hq */
+  int32_t n_kv_heads;  /* Hkv; g = Hq / Hkv query heads share one KV head (1 <= g <= 16);
+                          query head hq reads KV head hq / g */
+  int32_t batch;       /* B >= 1 */
+  int64_t capacity;    /* tokens per (b, h) stream, a positive multiple of 32 */
+  int32_t base_bits;   /* bits of the base key code: 2 */
+  int32_t group;       /* tokens per base-quantizer group: 32 */
+  int32_t rank;        /* r: 0, 4, 8, 16 or 32 (0 = base quantizer only) */
+  int32_t side_bits;   /* bits per side-code component: 4 */
+  int32_t key_dtype;   /* HEADQ_F32 or HEADQ_BF16: dtype of the keys given to append */
+  int32_t value_dtype; /* HEADQ_F32 or HEADQ_BF16: dtype of the values given to append, and of
+                          the dense value store */
+  int32_t value_mode;  /* HEADQ_V_DENSE or HEADQ_V_Q2 (2-bit values, d = 128 or 64) */
+  int32_t query_dtype; /* HEADQ_F32 or HEADQ_BF16: dtype of decode queries */
+} headq_config;
+
+typedef struct headq_cache { /* device pointers, layouts in the header comment above */
+  uint8_t* kcode;
+  uint16_t* kmeta;
+  uint8_t* scode;  /* may be NULL when rank == 0 */
+  uint16_t* ssc;   /* may be NULL when rank == 0 */
+  void* v;         /* dense values (value_mode == HEADQ_V_DENSE) */
+  uint8_t* vcode;  /* 2-bit values (value_mode == HEADQ_V_Q2) */
+  uint16_t* vmeta; /* 2-bit values (value_mode == HEADQ_V_Q2) */
+  const float* U;  /* [Hkv][d][r]; may be NULL when rank == 0 */
+} headq_cache;
+
+/*
+ * headq_calibrate — learn the side basis U_h from calibration queries (host only, synchronous).
+ * Summary §3 step 1: a rank-r basis per layer and head from PCA of post-RoPE calibration
+ * queries. This library's reading: one basis per KV head, pooling the g query heads that read
+ * it; the uncentered second moment (1/n) sum q q^T (the score error is q.e with the raw query);
+ * columns are the eigenvectors of the r largest eigenvalues in decreasing order, each signed so
+ * that its largest-magnitude entry (lowest index on ties) is positive. Computed in fp64
+ * (Householder tridiagonalization + implicit-shift QL).
+ *   q_cal  host f32 [Hq][n_cal][d], post-RoPE calibration queries (read only)
+ *   U      host f32 [Hkv][d][r] (written)
+ *   eig    host f64 [Hkv][r] eigenvalues (written; may be NULL)
+ * Errors: NULL, SHAPE (n_cal < 1, r > d), UNSUPPORTED (d, r), NUMERIC (non-finite input).
+ */
+headq_status headq_calibrate(const headq_config* cfg, const float* q_cal, int64_t n_cal, float* U,
+                             double* eig);
+
+/*
+ * headq_cache_append — quantize and store tokens [start, start + n_new) of every (b, h) stream.
+ * Summary §3 step 2: base-quantize each key with B_b, take the residual e = k - k_base,
+ * project it on U_h and side-quantize the projection with Q_q; the cache keeps the base key and
+ * the side code. This library's numerics (the integer results are bit-exact with a plain CPU
+ * evaluation of the same formulas):
+ *   per (32-token group, channel): s = fp16((max - min) / 3), z = fp16(min)
+ *   code = clamp(rint((k - z) * (1/s)), 0, 3)   (1/s = 0 when s == 0; ties to even)
+ *   e = k - fma(code, s, z)                      (f32)
+ *   y_i = sum_c U[c][i] e_c as one f32 fma chain over c = 0..d-1 starting from +0
+ *   sigma = fp16(max_i |y_i| / 7), zc_i = clamp(rint(y_i * (1/sigma)), -7, 7) (all 0 if sigma == 0)
+ * Dense values are copied into the cache layout; 2-bit values get the per-token quantizer over
+ * 32-channel groups with the same numerics.
+ *   k        device keys, key_dtype, element (b, h, t, c) at k[b*ks[0] + h*ks[1] + t*ks[2] + c]
+ *   k_strides element strides {batch, kv head, token}; channel stride is 1
+ *   v        device values (value_dtype; f32 or bf16 also in 2-bit mode), or NULL to leave the
+ *            value store untouched; v_strides as for keys (ignored when v is NULL)
+ *   start, n_new  token range of every stream; both multiples of 32, start + n_new <= capacity
+ * Errors: NULL, SHAPE, ALIGN (k, v and stride*element_size not multiples of 16 bytes, or
+ * start/n_new not multiples of 32), CAPACITY, UNSUPPORTED, HIP. n_new == 0 is a no-op.
+ */
+headq_status headq_cache_append(const headq_config* cfg, const headq_cache* cache, const void* k,
+                                const int64_t k_strides[3], const void* v, const int64_t v_strides[3],
+                                int64_t start, int64_t n_new, void* stream);
+
+/*
+ * headq_decode_attn — one decode step of attention for every (b, query head) over the first
+ * n_ctx cached tokens. Summary §3 step 3: the runtime query decodes the side code through
+ * U_h^T q and the corrected logit q.k_base/sqrt(d) + (U_h^T q).z_hat/sqrt(d) is taken directly,
+ * without rebuilding a full key; then softmax and the value readout sum_j p_j v_j (§1, §2.2).
+ * Computed in f32 with exact softmax over the n_ctx tokens, split over token ranges that are
+ * merged by log-sum-exp.
+ *   q           device [B][Hq][d] in query_dtype (contiguous)
+ *   n_ctx       tokens attended: a positive multiple of 32, <= capacity
+ *   out         device [B][Hq][d] in out_dtype (HEADQ_F32 or HEADQ_BF16), contiguous
+ *   corr_scale  multiplies the correction: 1 = HeadQ, 0 = base code only, -1 = wrong sign
+ *   logits_dbg  device f32 [B][Hq][n_ctx] corrected logits in natural-log units, or NULL
+ *   n_splits    token splits per (b, h); 0 = automatic, else 1..n_ctx/32
+ *   ws, ws_bytes  device workspace. With ws == NULL the call only stores the bytes it needs in
+ *               *ws_bytes and returns HEADQ_OK (nothing is launched). Otherwise *ws_bytes is
+ *               the size of ws.
+ * Errors: NULL, SHAPE, ALIGN, CAPACITY, WORKSPACE, UNSUPPORTED, HIP.
+ */
+headq_status headq_decode_attn(const headq_config* cfg, const headq_cache* cache, const void* q,
+                               int64_t n_ctx, void* out, int32_t out_dtype, float corr_scale, float* logits_dbg,
+                               int32_t n_splits, void* ws, size_t* ws_bytes, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* headq_status_string(headq_status s);
+
+/* ---- layout sizes in bytes (inline helpers, not exported) ---- */
+static inline size_t headq_kcode_bytes(const headq_config* c) {
+  return (size_t)c->batch * c->n_kv_heads * c->capacity * (c->head_dim / 4);
+}
+static inline size_t headq_kmeta_bytes(const headq_config* c) {
+  return (size_t)c->batch * c->n_kv_heads * (c->capacity / 32) * 2 * c->head_dim * 2;
+}
+static inline size_t headq_scode_bytes(const headq_config* c) {
+  return (size_t)c->batch * c->n_kv_heads * c->capacity * (c->rank / 2);
+}
+static inline size_t headq_ssc_bytes(const headq_config* c) {
+  return (size_t)c->batch * c->n_kv_heads * c->capacity * 2;
+}
+static inline size_t headq_v_bytes(const headq_config* c) {
+  return (size_t)c->batch * c->n_kv_heads * c->capacity * c->head_dim * (c->value_dtype == HEADQ_F32 ? 4 : 2);
+}
+static inline size_t headq_vcode_bytes(const headq_config* c) {
+  return (size_t)c->batch * c->n_kv_heads * c->capacity * (c->head_dim / 4);
+}
+static inline size_t headq_vmeta_bytes(const headq_config* c) {
+  return (size_t)c->batch * c->n_kv_heads * c->capacity * (c->head_dim / 32) * 2 * 2;
+}
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HEADQ_H */

@@ -1,0 +1,221 @@
+"""Thin Python binding of libheadq (ctypes): argument marshalling only.
+
+The three calls keep the C names: headq_calibrate, headq_cache_append, headq_decode_attn.
+PyTorch provides device memory and the current HIP stream; every step of the hot path runs in
+libheadq's HIP kernels. There is no fallback: if libheadq.so is missing or fails to load, every
+call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from pathlib import Path
+
+import numpy as np
+
+LIB_PATH = Path(__file__).resolve().parent / "libheadq.so"
+
+HEADQ_F32, HEADQ_BF16 = 0, 1
+HEADQ_V_DENSE, HEADQ_V_Q2 = 0, 1
+GROUP = 32
+
+STATUS = {
+    0: "HEADQ_OK", 1: "HEADQ_ERR_NULL", 2: "HEADQ_ERR_SHAPE", 3: "HEADQ_ERR_ALIGN", 4: "HEADQ_ERR_CAPACITY",
+    5: "HEADQ_ERR_WORKSPACE", 6: "HEADQ_ERR_NUMERIC", 7: "HEADQ_ERR_UNSUPPORTED", 8: "HEADQ_ERR_HIP",
+}
+EXPORTS = ("headq_calibrate", "headq_cache_append", "headq_decode_attn", "headq_status_string")
+
+
+class HeadQError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = status
+        super().__init__(f"{call} failed: {STATUS.get(status, status)} ({status_string(status)})")
+
+
+class headq_config(ctypes.Structure):
+    _fields_ = [
+        ("head_dim", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+        ("batch", ctypes.c_int32), ("capacity", ctypes.c_int64), ("base_bits", ctypes.c_int32),
+        ("group", ctypes.c_int32), ("rank", ctypes.c_int32), ("side_bits", ctypes.c_int32),
+        ("key_dtype", ctypes.c_int32), ("value_dtype", ctypes.c_int32), ("value_mode", ctypes.c_int32),
+        ("query_dtype", ctypes.c_int32),
+    ]
+
+
+class headq_cache(ctypes.Structure):
+    _fields_ = [
+        ("kcode", ctypes.c_void_p), ("kmeta", ctypes.c_void_p), ("scode", ctypes.c_void_p),
+        ("ssc", ctypes.c_void_p), ("v", ctypes.c_void_p), ("vcode", ctypes.c_void_p),
+        ("vmeta", ctypes.c_void_p), ("U", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load the in-tree libheadq.so (built by quantized_kv_cache_headq_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not LIB_PATH.exists():
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m quantized_kv_cache_headq_amd.build`")
+        L = ctypes.CDLL(str(LIB_PATH))
+        P, I32, I64, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+        L.headq_calibrate.argtypes = [P, P, I64, P, P]
+        L.headq_cache_append.argtypes = [P, P, P, P, P, P, I64, I64, P]
+        L.headq_decode_attn.argtypes = [P, P, P, I64, P, I32, F, P, I32, P, P, P]
+        L.headq_status_string.argtypes = [ctypes.c_int]
+        L.headq_status_string.restype = ctypes.c_char_p
+        for fn in ("headq_calibrate", "headq_cache_append", "headq_decode_attn"):
+            getattr(L, fn).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    try:
+        return load().headq_status_string(status).decode()
+    except Exception:
+        return STATUS.get(status, str(status))
+
+
+def _check(status: int, call: str):
+    if status != 0:
+        raise HeadQError(status, call)
+
+
+@dataclass
+class Config:
+    head_dim: int
+    n_q_heads: int
+    n_kv_heads: int
+    batch: int
+    capacity: int
+    rank: int
+    key_dtype: int = HEADQ_BF16
+    value_dtype: int = HEADQ_BF16
+    value_mode: int = HEADQ_V_DENSE
+    query_dtype: int = HEADQ_BF16
+    base_bits: int = 2
+    group: int = GROUP
+    side_bits: int = 4
+
+    def c(self) -> headq_config:
+        return headq_config(self.head_dim, self.n_q_heads, self.n_kv_heads, self.batch, self.capacity,
+                            self.base_bits, self.group, self.rank, self.side_bits, self.key_dtype,
+                            self.value_dtype, self.value_mode, self.query_dtype)
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, np.ndarray):
+        return t.ctypes.data
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+# ------------------------------------------------------------------------------------------------
+# the three calls
+
+def headq_calibrate(cfg: Config, q_cal: np.ndarray):
+    """Host PCA. q_cal: f32 [Hq][n_cal][d] (numpy). Returns (U f32 [Hkv][d][r], eig f64 [Hkv][r])."""
+    q = np.ascontiguousarray(q_cal, dtype=np.float32)
+    U = np.zeros((cfg.n_kv_heads, cfg.head_dim, cfg.rank), np.float32)
+    eig = np.zeros((cfg.n_kv_heads, cfg.rank), np.float64)
+    c = cfg.c()
+    _check(load().headq_calibrate(ctypes.byref(c), _ptr(q), q.shape[1], _ptr(U) if cfg.rank else None, _ptr(eig)),
+           "headq_calibrate")
+    return U, eig
+
+
+def _strides3(t):
+    if t.stride(-1) != 1:
+        raise ValueError("channel stride must be 1")
+    return (ctypes.c_int64 * 3)(t.stride(0), t.stride(1), t.stride(2))
+
+
+def headq_cache_append(cfg: Config, cache: headq_cache, k, v=None, start: int = 0, stream=None):
+    """Quantize and store k (and v) [B][Hkv][n_new][d] (torch device tensors) at token `start`."""
+    c = cfg.c()
+    ks = _strides3(k)
+    vs = _strides3(v) if v is not None else None
+    _check(load().headq_cache_append(ctypes.byref(c), ctypes.byref(cache), _ptr(k), ks, _ptr(v), vs, start,
+                                     k.shape[2], _stream(stream)), "headq_cache_append")
+
+
+def decode_workspace_bytes(cfg: Config, n_ctx: int, n_splits: int = 0) -> int:
+    c = cfg.c()
+    nbytes = ctypes.c_size_t(0)
+    _check(load().headq_decode_attn(ctypes.byref(c), None, None, n_ctx, None, 0, 1.0, None, n_splits, None,
+                                    ctypes.byref(nbytes), None), "headq_decode_attn(size query)")
+    return nbytes.value
+
+
+def headq_decode_attn(cfg: Config, cache: headq_cache, q, n_ctx: int, out, out_dtype: int = HEADQ_F32,
+                      corr_scale: float = 1.0, logits_dbg=None, n_splits: int = 0, ws=None, stream=None):
+    """One decode step: q [B][Hq][d] -> out [B][Hq][d] (torch device tensors); ws: a device buffer of at
+    least decode_workspace_bytes(cfg, n_ctx, n_splits) bytes."""
+    c = cfg.c()
+    nbytes = ctypes.c_size_t(ws.numel() * ws.element_size())
+    _check(load().headq_decode_attn(ctypes.byref(c), ctypes.byref(cache), _ptr(q), n_ctx, _ptr(out), out_dtype,
+                                    float(corr_scale), _ptr(logits_dbg), n_splits, _ptr(ws), ctypes.byref(nbytes),
+                                    _stream(stream)), "headq_decode_attn")
+
+
+# ------------------------------------------------------------------------------------------------
+# device buffers of one layer's cache (torch for memory only)
+
+class DeviceCache:
+    """Caller-owned device buffers of one layer in libheadq's cache format."""
+
+    def __init__(self, cfg: Config, device="cuda"):
+        import torch
+        self.cfg = cfg
+        B, H, cap, d, r = cfg.batch, cfg.n_kv_heads, cfg.capacity, cfg.head_dim, cfg.rank
+        u8, i16 = torch.uint8, torch.int16
+        self.kcode = torch.zeros((B, H, cap, d // 4), dtype=u8, device=device)
+        self.kmeta = torch.zeros((B, H, cap // GROUP, 2, d), dtype=i16, device=device)
+        self.scode = torch.zeros((B, H, cap, max(r // 2, 1)), dtype=u8, device=device) if r else None
+        self.ssc = torch.zeros((B, H, cap), dtype=i16, device=device) if r else None
+        self.v = self.vcode = self.vmeta = None
+        if cfg.value_mode == HEADQ_V_DENSE:
+            vdt = torch.float32 if cfg.value_dtype == HEADQ_F32 else torch.bfloat16
+            self.v = torch.zeros((B, H, cap // GROUP, d, GROUP), dtype=vdt, device=device)
+        else:
+            self.vcode = torch.zeros((B, H, cap // GROUP, d, 8), dtype=u8, device=device)
+            self.vmeta = torch.zeros((B, H, cap // GROUP, 2, d // GROUP, GROUP), dtype=i16, device=device)
+        self.U = None
+
+    def set_basis(self, U):
+        import torch
+        self.U = torch.as_tensor(np.ascontiguousarray(U, np.float32)).to(self.kcode.device)
+
+    def c(self) -> headq_cache:
+        return headq_cache(_ptr(self.kcode), _ptr(self.kmeta), _ptr(self.scode), _ptr(self.ssc), _ptr(self.v),
+                           _ptr(self.vcode), _ptr(self.vmeta), _ptr(self.U))
+
+    def append(self, k, v=None, start: int = 0, stream=None):
+        headq_cache_append(self.cfg, self.c(), k, v, start, stream)
+
+    def decode(self, q, n_ctx: int, out=None, out_dtype: int = HEADQ_F32, corr_scale: float = 1.0, logits_dbg=None,
+               n_splits: int = 0, ws=None, stream=None):
+        import torch
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32 if out_dtype == HEADQ_F32 else torch.bfloat16,
+                              device=q.device)
+        if ws is None:
+            nb = decode_workspace_bytes(self.cfg, n_ctx, n_splits)
+            ws = torch.empty((nb + 3) // 4, dtype=torch.float32, device=q.device)
+        headq_decode_attn(self.cfg, self.c(), q, n_ctx, out, out_dtype, corr_scale, logits_dbg, n_splits, ws, stream)
+        return out
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in (self.kcode, self.kmeta, self.scode, self.ssc, self.v,
+                                                           self.vcode, self.vmeta) if t is not None)

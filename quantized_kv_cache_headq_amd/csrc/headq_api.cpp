@@ -1,0 +1,216 @@
+// headq_api.cpp — the C ABI of libheadq: argument checks, split choice, kernel dispatch.
+//
+// Every check runs on the host before the first HIP call, so a rejected call enqueues nothing.
+// The library allocates no device memory: the caller passes the cache and the workspace.
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+
+#include "headq_internal.h"
+
+namespace {
+
+bool sync_debug() {
+  static const bool on = [] {
+    const char* s = std::getenv("HEADQ_SYNC_DEBUG");
+    return s && s[0] && std::strcmp(s, "0") != 0;
+  }();
+  return on;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+headq_status finish(hipError_t launched, hipStream_t stream) {
+  if (launched != hipSuccess) return HEADQ_ERR_HIP;
+  if (hipGetLastError() != hipSuccess) return HEADQ_ERR_HIP;
+  if (sync_debug()) {
+    if (hipStreamSynchronize(stream) != hipSuccess) return HEADQ_ERR_HIP;
+    if (hipGetLastError() != hipSuccess) return HEADQ_ERR_HIP;
+  }
+  return HEADQ_OK;
+}
+
+// Shape checks common to append and decode.
+headq_status check_config(const headq_config* c) {
+  if (!c) return HEADQ_ERR_NULL;
+  if (c->head_dim != 64 && c->head_dim != 128) return HEADQ_ERR_UNSUPPORTED;
+  if (c->n_q_heads < 1 || c->n_kv_heads < 1 || c->batch < 1 || c->capacity < 1) return HEADQ_ERR_SHAPE;
+  if (c->n_q_heads % c->n_kv_heads) return HEADQ_ERR_SHAPE;
+  if (c->n_q_heads / c->n_kv_heads > headq::kMaxGqa) return HEADQ_ERR_UNSUPPORTED;
+  if (c->capacity % headq::kGroup) return HEADQ_ERR_ALIGN;
+  if (c->base_bits != 2 || c->group != headq::kGroup || c->side_bits != 4) return HEADQ_ERR_UNSUPPORTED;
+  if (c->rank != 0 && c->rank != 4 && c->rank != 8 && c->rank != 16 && c->rank != 32) return HEADQ_ERR_UNSUPPORTED;
+  if ((c->key_dtype != HEADQ_F32 && c->key_dtype != HEADQ_BF16) ||
+      (c->value_dtype != HEADQ_F32 && c->value_dtype != HEADQ_BF16) ||
+      (c->query_dtype != HEADQ_F32 && c->query_dtype != HEADQ_BF16))
+    return HEADQ_ERR_UNSUPPORTED;
+  if (c->value_mode != HEADQ_V_DENSE && c->value_mode != HEADQ_V_Q2) return HEADQ_ERR_UNSUPPORTED;
+  return HEADQ_OK;
+}
+
+headq_status check_cache(const headq_config* c, const headq_cache* k) {
+  if (!k || !k->kcode || !k->kmeta) return HEADQ_ERR_NULL;
+  if (c->rank > 0 && (!k->scode || !k->ssc || !k->U)) return HEADQ_ERR_NULL;
+  if (c->value_mode == HEADQ_V_DENSE && !k->v) return HEADQ_ERR_NULL;
+  if (c->value_mode == HEADQ_V_Q2 && (!k->vcode || !k->vmeta)) return HEADQ_ERR_NULL;
+  const void* ptrs[] = {k->kcode, k->kmeta, k->scode, k->ssc, k->v, k->vcode, k->vmeta, k->U};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return HEADQ_ERR_ALIGN;
+  return HEADQ_OK;
+}
+
+}  // namespace
+
+extern "C" const char* headq_status_string(headq_status s) {
+  switch (s) {
+    case HEADQ_OK: return "ok";
+    case HEADQ_ERR_NULL: return "required pointer is NULL";
+    case HEADQ_ERR_SHAPE: return "inconsistent or out-of-range dimensions";
+    case HEADQ_ERR_ALIGN: return "token count/offset not a multiple of 32 or buffer not 16-byte aligned";
+    case HEADQ_ERR_CAPACITY: return "token range exceeds the cache capacity";
+    case HEADQ_ERR_WORKSPACE: return "workspace too small";
+    case HEADQ_ERR_NUMERIC: return "non-finite input";
+    case HEADQ_ERR_UNSUPPORTED: return "setting not supported by this build";
+    case HEADQ_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+extern "C" headq_status headq_cache_append(const headq_config* cfg, const headq_cache* cache, const void* k,
+                                           const int64_t k_strides[3], const void* v, const int64_t v_strides[3],
+                                           int64_t start, int64_t n_new, void* stream) {
+  headq_status st = check_config(cfg);
+  if (st != HEADQ_OK) return st;
+  if (!cache || !k || !k_strides) return HEADQ_ERR_NULL;
+  if (v && !v_strides) return HEADQ_ERR_NULL;
+  st = check_cache(cfg, cache);
+  if (st != HEADQ_OK) return st;
+  if (start < 0 || n_new < 0) return HEADQ_ERR_SHAPE;
+  if (start % headq::kGroup || n_new % headq::kGroup) return HEADQ_ERR_ALIGN;
+  if (start + n_new > cfg->capacity) return HEADQ_ERR_CAPACITY;
+  const int kes = cfg->key_dtype == HEADQ_F32 ? 4 : 2;
+  const int ves = cfg->value_dtype == HEADQ_F32 ? 4 : 2;
+  if (!aligned16(k)) return HEADQ_ERR_ALIGN;
+  for (int i = 0; i < 3; ++i) {
+    if (k_strides[i] < 0) return HEADQ_ERR_SHAPE;
+    if ((k_strides[i] * kes) % 16) return HEADQ_ERR_ALIGN;
+  }
+  if (k_strides[2] < cfg->head_dim) return HEADQ_ERR_SHAPE;
+  if (v) {
+    if (!aligned16(v)) return HEADQ_ERR_ALIGN;
+    for (int i = 0; i < 3; ++i) {
+      if (v_strides[i] < 0) return HEADQ_ERR_SHAPE;
+      if ((v_strides[i] * ves) % 16) return HEADQ_ERR_ALIGN;
+    }
+    if (v_strides[2] < cfg->head_dim) return HEADQ_ERR_SHAPE;
+  }
+  if (n_new == 0) return HEADQ_OK;
+
+  headq::AppendArgs a{};
+  a.d = cfg->head_dim;
+  a.r = cfg->rank;
+  a.hkv = cfg->n_kv_heads;
+  a.batch = cfg->batch;
+  a.cap = cfg->capacity;
+  a.start = start;
+  a.n_new = n_new;
+  a.key_bf16 = cfg->key_dtype == HEADQ_BF16;
+  a.value_bf16 = cfg->value_dtype == HEADQ_BF16;
+  a.value_mode = cfg->value_mode;
+  a.k = k;
+  a.ks_b = k_strides[0];
+  a.ks_h = k_strides[1];
+  a.ks_t = k_strides[2];
+  a.v = v;
+  if (v) {
+    a.vs_b = v_strides[0];
+    a.vs_h = v_strides[1];
+    a.vs_t = v_strides[2];
+  }
+  a.kcode = cache->kcode;
+  a.kmeta = cache->kmeta;
+  a.scode = cache->scode;
+  a.ssc = cache->ssc;
+  a.vdense = cache->v;
+  a.vcode = cache->vcode;
+  a.vmeta = cache->vmeta;
+  a.U = cache->U;
+  hipStream_t s = (hipStream_t)stream;
+  return finish(headq::launch_append(a, s), s);
+}
+
+namespace {
+
+// Token splits per (b, h) stream: enough workgroups to give every CU several, while keeping each
+// split at least a few groups long so the partial results stay a small fraction of the traffic.
+int auto_splits(const headq_config* c, int64_t n_groups) {
+  const int64_t streams = (int64_t)c->batch * c->n_kv_heads;
+  const int64_t target_wgs = 2048;
+  int64_t s = (target_wgs + streams - 1) / streams;
+  const int64_t min_groups_per_split = 4;
+  if (s * min_groups_per_split > n_groups) s = n_groups / min_groups_per_split;
+  if (s < 1) s = 1;
+  if (s > n_groups) s = n_groups;
+  return (int)s;
+}
+
+}  // namespace
+
+extern "C" headq_status headq_decode_attn(const headq_config* cfg, const headq_cache* cache, const void* q,
+                                          int64_t n_ctx, void* out, int32_t out_dtype, float corr_scale,
+                                          float* logits_dbg, int32_t n_splits, void* ws, size_t* ws_bytes,
+                                          void* stream) {
+  headq_status st = check_config(cfg);
+  if (st != HEADQ_OK) return st;
+  if (!ws_bytes) return HEADQ_ERR_NULL;
+  if (n_ctx < 1) return HEADQ_ERR_SHAPE;
+  if (n_ctx % headq::kGroup) return HEADQ_ERR_ALIGN;
+  if (n_ctx > cfg->capacity) return HEADQ_ERR_CAPACITY;
+  if (out_dtype != HEADQ_F32 && out_dtype != HEADQ_BF16) return HEADQ_ERR_UNSUPPORTED;
+  const int64_t n_groups = n_ctx / headq::kGroup;
+  if (n_splits < 0 || n_splits > n_groups) return HEADQ_ERR_SHAPE;
+  const int S = n_splits ? n_splits : auto_splits(cfg, n_groups);
+  const size_t need = headq::decode_ws_bytes(cfg->batch, cfg->n_q_heads, cfg->head_dim, S);
+  if (!ws) {
+    *ws_bytes = need;
+    return HEADQ_OK;
+  }
+  if (!cache || !q || !out) return HEADQ_ERR_NULL;
+  st = check_cache(cfg, cache);
+  if (st != HEADQ_OK) return st;
+  if (*ws_bytes < need) return HEADQ_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(out) || !aligned16(ws) || (logits_dbg && !aligned16(logits_dbg)))
+    return HEADQ_ERR_ALIGN;
+
+  headq::DecodeArgs a{};
+  a.d = cfg->head_dim;
+  a.r = cfg->rank;
+  a.hq = cfg->n_q_heads;
+  a.hkv = cfg->n_kv_heads;
+  a.batch = cfg->batch;
+  a.gqa = cfg->n_q_heads / cfg->n_kv_heads;
+  a.cap = cfg->capacity;
+  a.n_ctx = n_ctx;
+  a.n_splits = S;
+  a.groups_per_split = (int)((n_groups + S - 1) / S);
+  a.query_bf16 = cfg->query_dtype == HEADQ_BF16;
+  a.value_bf16 = cfg->value_dtype == HEADQ_BF16;
+  a.value_mode = cfg->value_mode;
+  a.out_bf16 = out_dtype == HEADQ_BF16;
+  a.corr_scale = corr_scale;
+  a.q = q;
+  a.kcode = cache->kcode;
+  a.kmeta = cache->kmeta;
+  a.scode = cache->scode;
+  a.ssc = cache->ssc;
+  a.vdense = cache->v;
+  a.vcode = cache->vcode;
+  a.vmeta = cache->vmeta;
+  a.U = cache->U;
+  a.logits_dbg = logits_dbg;
+  a.ws_o = (float*)ws;
+  a.ws_ml = (float*)ws + (size_t)cfg->batch * cfg->n_q_heads * S * cfg->head_dim;
+  a.out = out;
+  hipStream_t s = (hipStream_t)stream;
+  return finish(headq::launch_decode(a, s), s);
+}

@@ -1,0 +1,68 @@
+// headq_internal.h — launch descriptors shared by the host API and the HIP kernels of libheadq.
+// Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "headq.h"
+
+namespace headq {
+
+constexpr int kGroup = 32;     // tokens per base-quantizer group
+constexpr int kMaxGqa = 16;    // query heads per KV head supported by the decode kernels
+
+struct AppendArgs {
+  int d, r, hkv, batch;
+  int64_t cap;                 // tokens per stream in the cache
+  int64_t start, n_new;        // token range written (multiples of 32)
+  int key_bf16, value_bf16, value_mode;
+  const void* k;
+  int64_t ks_b, ks_h, ks_t;    // key element strides
+  const void* v;               // may be null: values untouched
+  int64_t vs_b, vs_h, vs_t;
+  uint8_t* kcode;
+  uint16_t* kmeta;
+  uint8_t* scode;
+  uint16_t* ssc;
+  void* vdense;
+  uint8_t* vcode;
+  uint16_t* vmeta;
+  const float* U;
+};
+
+struct DecodeArgs {
+  int d, r, hq, hkv, batch, gqa;
+  int64_t cap, n_ctx;
+  int n_splits;                // token splits per (b, h)
+  int groups_per_split;        // ceil(n_ctx / 32 / n_splits)
+  int query_bf16, value_bf16, value_mode, out_bf16;
+  float corr_scale;
+  const void* q;
+  const uint8_t* kcode;
+  const uint16_t* kmeta;
+  const uint8_t* scode;
+  const uint16_t* ssc;
+  const void* vdense;
+  const uint8_t* vcode;
+  const uint16_t* vmeta;
+  const float* U;
+  float* logits_dbg;           // may be null
+  float* ws_o;                 // [B][Hq][S][d]
+  float* ws_ml;                // [B][Hq][S][2]
+  void* out;
+};
+
+// Workspace bytes of a decode with these shapes.
+inline size_t decode_ws_bytes(int batch, int hq, int d, int n_splits) {
+  return (size_t)batch * hq * n_splits * (size_t)(d + 2) * sizeof(float);
+}
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+// Host eigensolver used by headq_calibrate (fp64, symmetric). Returns false on non-convergence.
+bool symmetric_eigen(int n, double* A, double* eigenvalues, double* eigenvectors);
+
+}  // namespace headq

@@ -1,0 +1,61 @@
+"""GPU parity at the full workload sizes, in the launch configuration the benchmark times.
+
+The oracle cannot decode a whole full-size batch in seconds, so it re-encodes a few sampled
+(b, h) streams itself from the generator (never from GPU output), and the GPU's cache bytes and
+outputs for those streams are compared with it.
+"""
+import numpy as np
+import pytest
+
+from oracle import oracle as orc
+from workloads import synth
+
+from .gpu_helpers import check_logits, check_out, decode_gpu, gpu_cache, host, say
+from .helpers import oracle_cache
+
+pytestmark = pytest.mark.gpu
+
+
+def _sampled(wname, streams, out_bf16=False):
+    w = synth.WORKLOADS[wname]
+    say("fullsize", wname, f"B={w.batch} T={w.n_ctx} streams={streams}")
+    U = orc.calibrate(synth.calibration_queries(w), w.n_kv_heads, w.rank)[0]
+    dc, K, V = gpu_cache(w, U)
+    q = synth.decode_queries(w)
+    lg, out = decode_gpu(dc, w, q, w.n_ctx, out_bf16=out_bf16)
+    g = w.gqa
+    for b, h in streams:
+        # oracle cache with a single batch row holding stream (b, h) at KV head h
+        kv = {(0, hh): (K[b, hh], V[b, hh]) for hh in range(w.n_kv_heads)}
+        wb = synth.scaled(w, batch=1)
+        oc, _ = oracle_cache(wb, U, batch=1, kv=kv)
+        for name in ("kcode", "kmeta", "scode", "ssc", "v", "vcode", "vmeta"):
+            if name in oc:
+                oc[name] = oc[name][:, h:h + 1]
+        heads = list(range(h * g, (h + 1) * g))
+        ref_l, ref_o = orc.decode(oc, q[b:b + 1, heads], U[h:h + 1], w.n_ctx, 1.0,
+                                  0 if w.value_mode == "dense" else 1, 0 if w.value_dtype == "f32" else 1)
+        check_logits(lg[b, heads], ref_l[0])
+        check_out(out[b, heads], ref_o[0], out_bf16)
+        compare_cache_stream(dc, oc, b, h)
+
+
+def compare_cache_stream(dc, oc_one, b, h):
+    """GPU stream (b, h) against the oracle's single-stream cache, bit for bit."""
+    for name in ("kcode", "kmeta", "scode", "ssc", "v", "vcode", "vmeta"):
+        t = getattr(dc, name)
+        if t is None or name not in oc_one:
+            continue
+        g = host(t[b:b + 1, h:h + 1])
+        o = oc_one[name]
+        if name == "v" and g.dtype == np.float32:
+            g, o = g.view(np.uint32), o.view(np.uint32)
+        assert np.array_equal(g, o), name
+
+
+def test_qwen7b_decode_full_size_sampled():
+    _sampled("qwen7b_decode", [(0, 0), (31, 3), (17, 2)])
+
+
+def test_tinyllama_decode_full_size_sampled():
+    _sampled("tinyllama_decode", [(0, 0), (15, 3)], out_bf16=True)

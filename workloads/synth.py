@@ -159,3 +159,23 @@ def scaled(w: Workload, **changes) -> Workload:
     d = {f: getattr(w, f) for f in w.__dataclass_fields__}
     d.update(changes)
     return Workload(**d)
+
+
+def stack_streams(w: Workload, kind: str, batch: int | None = None, T: int | None = None,
+                  workers: int = 8) -> np.ndarray:
+    """All (b, h) streams of `kind` ("keys" or "values") as f32 [B][Hkv][T][d], generated in a
+    thread pool (each stream is seeded on its own, so the result does not depend on `workers`)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    B = w.batch if batch is None else batch
+    T = w.n_ctx if T is None else T
+    fn = keys if kind == "keys" else values
+    out = np.empty((B, w.n_kv_heads, T, w.head_dim), np.float32)
+
+    def one(bh):
+        b, h = divmod(bh, w.n_kv_heads)
+        out[b, h] = fn(w, b, h, T)
+
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(one, range(B * w.n_kv_heads)))
+    return out
