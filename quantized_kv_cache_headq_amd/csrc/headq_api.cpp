@@ -141,14 +141,25 @@ extern "C" headq_status headq_cache_append(const headq_config* cfg, const headq_
 
 namespace {
 
-// Token splits per (b, h) stream: enough workgroups to give every CU several, while keeping each
-// split at least a few groups long so the partial results stay a small fraction of the traffic.
-int auto_splits(const headq_config* c, int64_t n_groups) {
+// The matrix-core kernel handles dense bf16 values; HEADQ_DECODE_KERNEL=valu selects the plain
+// vector kernel instead (kept as the measured comparison and for f32 / 2-bit values).
+bool decode_uses_mfma(const headq_config* c) {
+  static const bool force_valu = [] {
+    const char* s = std::getenv("HEADQ_DECODE_KERNEL");
+    return s && std::strcmp(s, "valu") == 0;
+  }();
+  return !force_valu && c->value_mode == HEADQ_V_DENSE && c->value_dtype == HEADQ_BF16;
+}
+
+// Token splits per (b, h) stream: about 2048 waves over the 256 CUs, with every chunk (the
+// groups one wave walks) at least 4 groups long so the partials stay a small fraction of the
+// traffic.
+int auto_splits(const headq_config* c, int64_t n_groups, int chunks) {
   const int64_t streams = (int64_t)c->batch * c->n_kv_heads;
-  const int64_t target_wgs = 2048;
-  int64_t s = (target_wgs + streams - 1) / streams;
-  const int64_t min_groups_per_split = 4;
-  if (s * min_groups_per_split > n_groups) s = n_groups / min_groups_per_split;
+  const int64_t target_waves = 2048;
+  int64_t s = (target_waves + streams * chunks - 1) / (streams * chunks);
+  const int64_t min_groups_per_chunk = 4;
+  if (s * chunks * min_groups_per_chunk > n_groups) s = n_groups / (chunks * min_groups_per_chunk);
   if (s < 1) s = 1;
   if (s > n_groups) s = n_groups;
   return (int)s;
@@ -169,7 +180,9 @@ extern "C" headq_status headq_decode_attn(const headq_config* cfg, const headq_c
   if (out_dtype != HEADQ_F32 && out_dtype != HEADQ_BF16) return HEADQ_ERR_UNSUPPORTED;
   const int64_t n_groups = n_ctx / headq::kGroup;
   if (n_splits < 0 || n_splits > n_groups) return HEADQ_ERR_SHAPE;
-  const int S = n_splits ? n_splits : auto_splits(cfg, n_groups);
+  const bool mfma = decode_uses_mfma(cfg);
+  const int chunks = mfma ? 4 : 1;
+  const int S = n_splits ? n_splits : auto_splits(cfg, n_groups, chunks);
   const size_t need = headq::decode_ws_bytes(cfg->batch, cfg->n_q_heads, cfg->head_dim, S);
   if (!ws) {
     *ws_bytes = need;
@@ -192,7 +205,9 @@ extern "C" headq_status headq_decode_attn(const headq_config* cfg, const headq_c
   a.cap = cfg->capacity;
   a.n_ctx = n_ctx;
   a.n_splits = S;
-  a.groups_per_split = (int)((n_groups + S - 1) / S);
+  a.chunks_per_split = chunks;
+  a.use_mfma = mfma;
+  a.groups_per_split = (int)((n_groups + (int64_t)S * chunks - 1) / ((int64_t)S * chunks));
   a.query_bf16 = cfg->query_dtype == HEADQ_BF16;
   a.value_bf16 = cfg->value_dtype == HEADQ_BF16;
   a.value_mode = cfg->value_mode;

@@ -35,8 +35,10 @@ struct AppendArgs {
 struct DecodeArgs {
   int d, r, hq, hkv, batch, gqa;
   int64_t cap, n_ctx;
-  int n_splits;                // token splits per (b, h)
-  int groups_per_split;        // ceil(n_ctx / 32 / n_splits)
+  int n_splits;                // token splits (workgroups) per (b, h); one partial result each
+  int groups_per_split;        // 32-token groups per chunk; a split has chunks_per_split chunks
+  int chunks_per_split;        // 1 (VALU kernel) or 4 (MFMA kernel: one chunk per wave)
+  int use_mfma;                // matrix-core kernel (dense bf16 values)
   int query_bf16, value_bf16, value_mode, out_bf16;
   float corr_scale;
   const void* q;
@@ -61,6 +63,7 @@ inline size_t decode_ws_bytes(int batch, int hq, int d, int n_splits) {
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_mfma_split(const DecodeArgs& a, hipStream_t stream);
 
 // Host eigensolver used by headq_calibrate (fp64, symmetric). Returns false on non-convergence.
 bool symmetric_eigen(int n, double* A, double* eigenvalues, double* eigenvectors);

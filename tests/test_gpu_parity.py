@@ -99,6 +99,10 @@ def test_strided_keys_and_values():
 
 
 def test_split_count_invariance_and_determinism():
+    """Splitting the tokens differently only changes rounding. The matrix-core path carries each
+    probability as bf16 hi + lo (relative representation error <= 2^-18), so two split counts may
+    differ by up to 2 * max|v| * 2^-18 (plus f32 accumulation rounding); the same split count is
+    bit-stable."""
     w = synth.scaled(W["qwen7b_decode"], n_q_heads=14, n_kv_heads=2)
     U = orc.calibrate(synth.calibration_queries(w, n_cal=128), 2, w.rank)[0]
     say("splits", w.name)
@@ -107,7 +111,8 @@ def test_split_count_invariance_and_determinism():
     _, ref = decode_gpu(dc, w, q, 2048, n_splits=1, logits=False)
     for s in (2, 7, 16, 64):
         _, o = decode_gpu(dc, w, q, 2048, n_splits=s, logits=False)
-        assert np.allclose(o, ref, rtol=1e-5, atol=1e-6), s
+        bound = 2 * float(np.abs(V).max()) * 2.0 ** -18 + 2e-6
+        assert np.max(np.abs(o - ref)) <= bound, (s, np.max(np.abs(o - ref)), bound)
     _, a = decode_gpu(dc, w, q, 2048, logits=False)
     for _ in range(3):
         _, b = decode_gpu(dc, w, q, 2048, logits=False)
