@@ -25,7 +25,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 METRIC = "decode-attn cached tokens·heads/s + achieved HBM GB/s (% of peak), 1 GPU"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_qwen7b_traffic.json")
-DECODE_SRC = os.path.join(ROOT, "quantized_kv_cache_headq_amd", "csrc", "decode.hip")
+DECODE_SRC = os.path.join(ROOT, "quantized_kv_cache_headq_amd", "csrc", "decode_mfma.hip")
 
 
 def algorithmic_bytes_per_token_head(w) -> int:
@@ -150,7 +150,7 @@ def main():
     k_new, v_new = K[:, :, last:], V[:, :, last:]
     out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
     ws_bytes = hq.decode_workspace_bytes(cfg, n_ctx, args.splits)
-    ws = torch.empty((ws_bytes + 3) // 4, dtype=torch.float32, device=dev)
+    ws = torch.zeros((ws_bytes + 3) // 4, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
     if args.copy_probe:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
@@ -220,7 +220,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "headq_decode_attn (split kernel + merge kernel, timed together)",
+            "kernel": "headq_decode_attn (one launch: decode_mfma_kernel, splits merged in-kernel)",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

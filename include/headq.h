@@ -109,7 +109,7 @@ typedef struct headq_cache { /* device pointers, layouts in the header comment a
  * it; the uncentered second moment (1/n) sum q q^T (the score error is q.e with the raw query);
  * columns are the eigenvectors of the r largest eigenvalues in decreasing order, each signed so
  * that its largest-magnitude entry (lowest index on ties) is positive. Computed in fp64
- * (Householder tridiagonalization + implicit-shift QL).
+ * (Householder tridiagonalization + implicit symmetric QR with Wilkinson shifts).
  *   q_cal  host f32 [Hq][n_cal][d], post-RoPE calibration queries (read only)
  *   U      host f32 [Hkv][d][r] (written)
  *   eig    host f64 [Hkv][r] eigenvalues (written; may be NULL)
@@ -155,10 +155,13 @@ headq_status headq_cache_append(const headq_config* cfg, const headq_cache* cach
  *   out         device [B][Hq][d] in out_dtype (HEADQ_F32 or HEADQ_BF16), contiguous
  *   corr_scale  multiplies the correction: 1 = HeadQ, 0 = base code only, -1 = wrong sign
  *   logits_dbg  device f32 [B][Hq][n_ctx] corrected logits in natural-log units, or NULL
- *   n_splits    token splits per (b, h); 0 = automatic, else 1..n_ctx/32
+ *   n_splits    token splits per (b, h); 0 = automatic, else 1..n_ctx/32 (at most 128 with
+ *               dense bf16 values)
  *   ws, ws_bytes  device workspace. With ws == NULL the call only stores the bytes it needs in
  *               *ws_bytes and returns HEADQ_OK (nothing is launched). Otherwise *ws_bytes is
- *               the size of ws.
+ *               the size of ws. The workspace must be zero-filled before its first use; every
+ *               call leaves its leading counter region zero again, so one zeroed workspace
+ *               serves any number of calls. Calls that share a workspace must not overlap.
  * Errors: NULL, SHAPE, ALIGN, CAPACITY, WORKSPACE, UNSUPPORTED, HIP.
  */
 headq_status headq_decode_attn(const headq_config* cfg, const headq_cache* cache, const void* q,

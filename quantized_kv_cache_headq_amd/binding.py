@@ -160,8 +160,8 @@ def decode_workspace_bytes(cfg: Config, n_ctx: int, n_splits: int = 0) -> int:
 
 def headq_decode_attn(cfg: Config, cache: headq_cache, q, n_ctx: int, out, out_dtype: int = HEADQ_F32,
                       corr_scale: float = 1.0, logits_dbg=None, n_splits: int = 0, ws=None, stream=None):
-    """One decode step: q [B][Hq][d] -> out [B][Hq][d] (torch device tensors); ws: a device buffer of at
-    least decode_workspace_bytes(cfg, n_ctx, n_splits) bytes."""
+    """One decode step: q [B][Hq][d] -> out [B][Hq][d] (torch device tensors); ws: a zero-filled device
+    buffer of at least decode_workspace_bytes(cfg, n_ctx, n_splits) bytes (calls keep it reusable)."""
     c = cfg.c()
     nbytes = ctypes.c_size_t(ws.numel() * ws.element_size())
     _check(load().headq_decode_attn(ctypes.byref(c), ctypes.byref(cache), _ptr(q), n_ctx, _ptr(out), out_dtype,
@@ -212,7 +212,7 @@ class DeviceCache:
                               device=q.device)
         if ws is None:
             nb = decode_workspace_bytes(self.cfg, n_ctx, n_splits)
-            ws = torch.empty((nb + 3) // 4, dtype=torch.float32, device=q.device)
+            ws = torch.zeros((nb + 3) // 4, dtype=torch.float32, device=q.device)
         headq_decode_attn(self.cfg, self.c(), q, n_ctx, out, out_dtype, corr_scale, logits_dbg, n_splits, ws, stream)
         return out
 

@@ -266,12 +266,7 @@ hipError_t launch_split(const DecodeArgs& a, hipStream_t s) {
 template <int D>
 hipError_t launch_d(const DecodeArgs& a, hipStream_t s) {
   hipError_t e;
-  if (a.use_mfma) {
-    e = launch_decode_mfma_split(a, s);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_reduce_kernel<D>), dim3((unsigned)a.hq, (unsigned)a.batch), dim3(D), 0, s, a);
-    return hipGetLastError();
-  }
+  if (a.use_mfma) return launch_decode_mfma_split(a, s);  // merges the splits itself
   switch (a.r) {
     case 0: e = launch_split<D, 0>(a, s); break;
     case 4: e = launch_split<D, 4>(a, s); break;

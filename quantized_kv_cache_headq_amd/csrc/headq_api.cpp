@@ -183,7 +183,8 @@ extern "C" headq_status headq_decode_attn(const headq_config* cfg, const headq_c
   const bool mfma = decode_uses_mfma(cfg);
   const int chunks = mfma ? 4 : 1;
   const int S = n_splits ? n_splits : auto_splits(cfg, n_groups, chunks);
-  const size_t need = headq::decode_ws_bytes(cfg->batch, cfg->n_q_heads, cfg->head_dim, S);
+  if (mfma && S > headq::kMaxSplitsMfma) return HEADQ_ERR_UNSUPPORTED;
+  const size_t need = headq::decode_ws_bytes(cfg->batch, cfg->n_q_heads, cfg->n_kv_heads, cfg->head_dim, S);
   if (!ws) {
     *ws_bytes = need;
     return HEADQ_OK;
@@ -223,8 +224,9 @@ extern "C" headq_status headq_decode_attn(const headq_config* cfg, const headq_c
   a.vmeta = cache->vmeta;
   a.U = cache->U;
   a.logits_dbg = logits_dbg;
-  a.ws_o = (float*)ws;
-  a.ws_ml = (float*)ws + (size_t)cfg->batch * cfg->n_q_heads * S * cfg->head_dim;
+  a.ws_count = (uint32_t*)ws;
+  a.ws_o = (float*)((char*)ws + headq::decode_ws_counter_bytes(cfg->batch, cfg->n_kv_heads));
+  a.ws_ml = a.ws_o + (size_t)cfg->batch * cfg->n_q_heads * S * cfg->head_dim;
   a.out = out;
   hipStream_t s = (hipStream_t)stream;
   return finish(headq::launch_decode(a, s), s);

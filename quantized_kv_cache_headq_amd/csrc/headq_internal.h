@@ -12,6 +12,8 @@ namespace headq {
 
 constexpr int kGroup = 32;     // tokens per base-quantizer group
 constexpr int kMaxGqa = 16;    // query heads per KV head supported by the decode kernels
+constexpr int kMaxSplitsMfma = 128;  // splits per stream of the matrix-core decode (its in-kernel
+                                     // merge stages 2 * splits * g floats in LDS)
 
 struct AppendArgs {
   int d, r, hkv, batch;
@@ -51,14 +53,19 @@ struct DecodeArgs {
   const uint16_t* vmeta;
   const float* U;
   float* logits_dbg;           // may be null
+  uint32_t* ws_count;          // [B][Hkv] arrival counters (zero between calls)
   float* ws_o;                 // [B][Hq][S][d]
   float* ws_ml;                // [B][Hq][S][2]
   void* out;
 };
 
-// Workspace bytes of a decode with these shapes.
-inline size_t decode_ws_bytes(int batch, int hq, int d, int n_splits) {
-  return (size_t)batch * hq * n_splits * (size_t)(d + 2) * sizeof(float);
+// Workspace of a decode: per-(b, h) arrival counters (rounded up to 256 bytes), then the split
+// partials (unnormalised outputs, then running max and sum).
+inline size_t decode_ws_counter_bytes(int batch, int hkv) {
+  return ((size_t)batch * hkv * sizeof(uint32_t) + 255) / 256 * 256;
+}
+inline size_t decode_ws_bytes(int batch, int hq, int hkv, int d, int n_splits) {
+  return decode_ws_counter_bytes(batch, hkv) + (size_t)batch * hq * n_splits * (size_t)(d + 2) * sizeof(float);
 }
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);

@@ -117,3 +117,26 @@ def test_split_count_invariance_and_determinism():
     for _ in range(3):
         _, b = decode_gpu(dc, w, q, 2048, logits=False)
         assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_workspace_counters_return_to_zero_and_reuse():
+    """The split merge counts workgroups in on the workspace; every call must leave the counter
+    region zero so one zeroed workspace serves calls with different split counts."""
+    import torch
+    import quantized_kv_cache_headq_amd as hq
+    w = synth.scaled(W["qwen7b_decode"], n_q_heads=14, n_kv_heads=2)
+    U = orc.calibrate(synth.calibration_queries(w, n_cal=128), 2, w.rank)[0]
+    say("workspace reuse", w.name)
+    dc, K, V = gpu_cache(w, U, 2, 1024)
+    q = synth.decode_queries(w, batch=2)
+    from .gpu_helpers import to_device
+    qd = to_device(q, "bf16")
+    nb = max(hq.decode_workspace_bytes(dc.cfg, 1024, s) for s in (1, 3, 8, 32))
+    ws = torch.zeros((nb + 3) // 4, dtype=torch.float32, device="cuda")
+    oc = oracle_for(w, U, K, V, 1024)
+    _, ref = orc.decode(oc, q, U, 1024, 1.0, 0, 1, want_logits=False)
+    for s in (1, 3, 8, 32, 0, 3):
+        out = dc.decode(qd, 1024, n_splits=s, ws=ws)
+        torch.cuda.synchronize()
+        check_out(out.cpu().numpy(), ref, False)
+        assert int(ws[:64].abs().sum().item()) == 0, f"counters not reset after n_splits={s}"

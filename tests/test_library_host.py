@@ -169,7 +169,7 @@ def test_decode_workspace_query_and_validation():
     st, nb = _decode_status(cfg, ws=None, nbytes=0)
     assert st == 0 and nb > 0
     st1, nb1 = _decode_status(cfg, ws=None, nbytes=0, n_splits=1)
-    assert st1 == 0 and nb1 == 2 * 4 * 1 * (64 + 2) * 4
+    assert st1 == 0 and nb1 == 256 + 2 * 4 * 1 * (64 + 2) * 4  # counters (padded), then partials
     assert _decode_status(cfg, nbytes=nb1 - 4, n_splits=1)[0] == 5           # workspace too small
     assert _decode_status(cfg, n_ctx=48)[0] == 3                              # n_ctx % 32
     assert _decode_status(cfg, n_ctx=160)[0] == 4                             # n_ctx > capacity
@@ -178,4 +178,4 @@ def test_decode_workspace_query_and_validation():
     assert _decode_status(cfg, q=0x30000002)[0] == 3                          # misaligned query
     assert _decode_status(cfg, out_dtype=5)[0] == 7
     assert _decode_status(cfg, q=None)[0] == 1
-    assert hq.decode_workspace_bytes(cfg, 64, 2) == 2 * 4 * 2 * 66 * 4
+    assert hq.decode_workspace_bytes(cfg, 64, 2) == 256 + 2 * 4 * 2 * 66 * 4
