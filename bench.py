@@ -1,14 +1,16 @@
-"""Benchmark of the HeadQ decode hot path on one MI355X.
+"""Benchmark of the HeadQ hot path on one MI355X.
 
 python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload qwen7b_decode] [--no-cpu-baseline]
 
-One step = one decode step of the workload through libheadq: headq_cache_append of the newest
-32-token group of every (b, h) stream, then headq_decode_attn over the whole context. The
-calibration (host PCA) runs once before timing, as the method prescribes (offline), and is
+Decode workloads (qwen7b_decode, the default; tinyllama_decode; qwen14b_fullkv): one step is one
+decode step through libheadq, per layer headq_cache_append of the newest 32-token group of every
+(b, h) stream, then headq_decode_attn over the whole context (tinyllama_decode runs its 22 layers,
+each on its own cache). append_prefill: one step is headq_cache_append of the whole prefill.
+The calibration (host PCA) runs once before timing, as the method prescribes (offline), and is
 reported separately. Inputs are seeded synthetic tensors resident in HBM before timing starts;
 several cache copies are rotated so the 256 MB MALL cannot hold the working set.
 
-Prints one JSON line (rank 0).
+Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -23,6 +25,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+FP32_VECTOR_PEAK_TFLOPS = 157.3     # 256 CU x 64 lanes x 2 (packed pair) x 2 flop per fma x 2.4 GHz
+FP32_NONPACKED_PEAK_TFLOPS = 78.6   # the same without packed-fp32 instructions
 METRIC = "decode-attn cached tokens·heads/s + achieved HBM GB/s (% of peak), 1 GPU"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_qwen7b_traffic.json")
 DECODE_SRC = os.path.join(ROOT, "quantized_kv_cache_headq_amd", "csrc", "decode_mfma.hip")
@@ -37,6 +41,30 @@ def algorithmic_bytes_per_token_head(w) -> int:
     else:
         v = d // 4 + d // 8  # 2-bit codes, fp16 step/zero per 32 channels
     return k + v
+
+
+def append_bytes(w) -> int:
+    """Bytes per token per KV head of a key append: keys in, codes, step/zero, nibbles, sigma out."""
+    d, r = w.head_dim, w.rank
+    kin = d * (4 if w.key_dtype == "f32" else 2)
+    return kin + d // 4 + d // 8 + r // 2 + (2 if r else 0)
+
+
+def copy_ceiling(torch, dev, stream) -> float:
+    """Read+write GB/s of a 1 GiB device-to-device copy (torch's copy kernel) on the same stream."""
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    gbs = 10 * 2 * src.numel() * 4 / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del src, dst
+    return gbs
 
 
 def source_sha() -> str:
@@ -142,70 +170,105 @@ def main():
     t0 = time.perf_counter()
     U, _ = hq.headq_calibrate(cfg, qcal)
     calib_s = time.perf_counter() - t0
+    append_only = w.name == "append_prefill"
     K = torch.from_numpy(synth.stack_streams(w, "keys", workers=16)).to(dev).to(tdt[w.key_dtype])
-    V = torch.from_numpy(synth.stack_streams(w, "values", workers=16)).to(dev).to(tdt[w.value_dtype])
+    V = None if append_only else torch.from_numpy(synth.stack_streams(w, "values", workers=16)).to(dev).to(
+        tdt[w.value_dtype])
     q = torch.from_numpy(synth.decode_queries(w)).to(dev).to(tdt[w.query_dtype])
+    n_layers = w.layers
     caches = []
-    for _ in range(args.copies):
+    n_copies = max(args.copies, n_layers, 4 if append_only else 1)
+    for _ in range(n_copies):
         dc = hq.DeviceCache(cfg, device=dev)
         dc.set_basis(U)
         dc.append(K, V, 0)
         caches.append(dc)
     n_ctx = w.n_ctx
     last = n_ctx - 32
-    k_new, v_new = K[:, :, last:], V[:, :, last:]
+    k_new = K[:, :, last:]
+    v_new = None if V is None else V[:, :, last:]
     out = torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
     ws_bytes = hq.decode_workspace_bytes(cfg, n_ctx, args.splits)
     ws = torch.zeros((ws_bytes + 3) // 4, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
+    copy_gbs = copy_ceiling(torch, dev, stream)
     if args.copy_probe:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         dst.copy_(src)
     torch.cuda.synchronize()
-    del K, V
+    if append_only:
+        # a prefill's keys are read once: rotate copies so the 256 MB MALL cannot serve them
+        Ks = [K] + [K.clone() for _ in range(n_copies - 1)]
+    else:
+        del K, V
 
-    def step(i):
-        dc = caches[i % len(caches)]
-        dc.append(k_new, v_new, last, stream=stream)
-        dc.decode(q, n_ctx, out=out, out_dtype=hq.HEADQ_BF16, n_splits=args.splits, ws=ws, stream=stream)
+    # One step: decode workloads append the newest 32-token group of every stream and decode over
+    # the whole context, once per layer (each layer its own cache); the prefill workload appends
+    # the whole prefill.
+    def run(i, marks=None):
+        if append_only:
+            dc = caches[i % len(caches)]
+            if marks:
+                marks[0].record(stream)
+            dc.append(Ks[i % len(Ks)], None, 0, stream=stream)
+            if marks:
+                marks[1].record(stream)
+            return
+        for l in range(n_layers):
+            dc = caches[(i * n_layers + l) % len(caches)]
+            if marks:
+                marks[2 * l].record(stream)
+            dc.append(k_new, v_new, last, stream=stream)
+            if marks:
+                marks[2 * l + 1].record(stream)
+            dc.decode(q, n_ctx, out=out, out_dtype=hq.HEADQ_BF16, n_splits=args.splits, ws=ws, stream=stream)
+        if marks:
+            marks[-1].record(stream)
 
     for i in range(args.warmup):
-        step(i)
+        run(i)
     torch.cuda.synchronize()
 
     # ---- timed region: events on the stream the kernels run on
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    n_marks = 2 if append_only else 2 * n_layers + 1
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n_marks)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(args.steps):
-        dc = caches[i % len(caches)]
-        e0, e1, e2 = ev[i]
-        e0.record(stream)
-        dc.append(k_new, v_new, last, stream=stream)
-        e1.record(stream)
-        dc.decode(q, n_ctx, out=out, out_dtype=hq.HEADQ_BF16, n_splits=args.splits, ws=ws, stream=stream)
-        e2.record(stream)
+        run(i, ev[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
-    append_ms = np.array([e0.elapsed_time(e1) for e0, e1, _ in ev])
-    decode_ms = np.array([e1.elapsed_time(e2) for _, e1, e2 in ev])
-    step_ms = np.array([e0.elapsed_time(e2) for e0, _, e2 in ev])
+    step_ms = np.array([m[0].elapsed_time(m[-1]) for m in ev])
     ms_per_step = float(step_ms.mean())
+    if append_only:
+        append_ms = step_ms
+        decode_ms = None
+    else:
+        append_ms = np.array([[m[2 * l].elapsed_time(m[2 * l + 1]) for l in range(n_layers)] for m in ev])
+        decode_ms = np.array([[m[2 * l + 1].elapsed_time(m[2 * l + 2]) for l in range(n_layers)] for m in ev])
 
-    tok_heads = w.batch * w.n_q_heads * n_ctx
-    value = tok_heads / (ms_per_step / 1e3)
-    per_tok = algorithmic_bytes_per_token_head(w)
-    alg_bytes = per_tok * w.batch * w.n_kv_heads * n_ctx
-    dec_s = float(decode_ms.mean()) / 1e3
-    achieved = alg_bytes / dec_s / 1e9
-    traffic = traffic_per_launch()
-
+    kinds = {"f32": "f32", "bf16": "bf16"}
+    desc = {
+        "tinyllama_decode": "TinyLlama-1.1B-shaped decode",
+        "qwen7b_decode": "Qwen2.5-7B-shaped decode",
+        "qwen14b_fullkv": "Qwen2.5-14B-shaped full-KV 2-bit decode",
+        "append_prefill": "cache write of a prefill",
+        "tiny": "tiny decode",
+    }[w.name]
+    config = {
+        "workload": f"{w.name}: {desc}, Hq {w.n_q_heads}, Hkv {w.n_kv_heads}, d {w.head_dim}, batch {w.batch}, "
+                    f"context {n_ctx}, 2-bit keys + rank-{w.rank} 4-bit side code"
+                    + ("" if append_only else f", {w.value_mode} {kinds[w.value_dtype]} values")
+                    + (f", {n_layers} layers" if n_layers > 1 else ""),
+        "batch": w.batch, "n_ctx": n_ctx, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
+        "head_dim": w.head_dim, "rank": w.rank, "layers": n_layers,
+        "step": ("headq_cache_append of the whole prefill (keys)" if append_only else
+                 "per layer: append newest 32-token group + decode over the full context"),
+        "cache_copies": len(caches), "n_splits": args.splits or "auto",
+    }
     result = {
         "metric": METRIC,
-        "value": value,
-        "unit": "query-head cached tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -215,34 +278,56 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {
-            "workload": f"{w.name}: Qwen2.5-7B-shaped decode, Hq {w.n_q_heads}, Hkv {w.n_kv_heads}, d {w.head_dim}, "
-                        f"batch {w.batch}, context {n_ctx}, 2-bit keys + rank-{w.rank} 4-bit side code, "
-                        f"{w.value_mode} {w.value_dtype} values" if w.name == "qwen7b_decode" else w.name,
-            "batch": w.batch, "n_ctx": n_ctx, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
-            "head_dim": w.head_dim, "rank": w.rank, "io": "bf16 queries/keys/values, bf16 output",
-            "step": "append newest 32-token group + decode over the full context",
-            "cache_copies": len(caches), "n_splits": args.splits or "auto",
-        },
-        "roofline": {
-            "bound": "hbm",
-            "kernel": "headq_decode_attn (one launch: decode_mfma_kernel, splits merged in-kernel)",
-            "achieved": achieved,
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS,
-            "traffic": traffic,
-            "algorithmic_bytes_per_launch": alg_bytes,
-            "bytes_per_token_kv_head": per_tok,
-        },
-        "decode_ms": float(decode_ms.mean()),
-        "decode_ms_p10_p90": [float(np.percentile(decode_ms, 10)), float(np.percentile(decode_ms, 90))],
-        "append_ms": float(append_ms.mean()),
-        "kv_head_tokens_per_s": w.batch * w.n_kv_heads * n_ctx / (ms_per_step / 1e3),
-        "calibrate_s_host": calib_s,
-        "wall_s_timed": wall,
+        "config": config,
     }
-    if not args.no_cpu_baseline:
+    if append_only:
+        tok_heads = w.batch * w.n_kv_heads * n_ctx
+        flops = 2 * w.rank * w.head_dim * tok_heads
+        achieved = flops / (ms_per_step / 1e3) / 1e12
+        result.update({
+            "metric": "cache-append tokens·KV-heads/s, 1 GPU",
+            "value": tok_heads / (ms_per_step / 1e3),
+            "unit": "KV-head tokens/s",
+            "roofline": {
+                "bound": "alu", "kernel": "append_keys_kernel (one launch)",
+                "achieved": achieved, "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / FP32_VECTOR_PEAK_TFLOPS, "traffic": None,
+                "peak_nonpacked": FP32_NONPACKED_PEAK_TFLOPS,
+                "frac_nonpacked": achieved / FP32_NONPACKED_PEAK_TFLOPS,
+                "algorithmic_flops_per_launch": flops,
+                "hbm_gbs": append_bytes(w) * tok_heads / (ms_per_step / 1e3) / 1e9,
+            },
+        })
+    else:
+        tok_heads = w.batch * w.n_q_heads * n_ctx * n_layers
+        per_tok = algorithmic_bytes_per_token_head(w)
+        alg_bytes = per_tok * w.batch * w.n_kv_heads * n_ctx
+        dec_s = float(decode_ms.mean()) / 1e3
+        achieved = alg_bytes / dec_s / 1e9
+        mfma = w.value_mode == "dense" and w.value_dtype == "bf16"
+        traffic = traffic_per_launch() if w.name == "qwen7b_decode" else None
+        result.update({
+            "value": tok_heads / (ms_per_step / 1e3),
+            "unit": "query-head cached tokens/s",
+            "roofline": {
+                "bound": "hbm",
+                "kernel": ("headq_decode_attn (one launch: decode_mfma_kernel, splits merged in-kernel)" if mfma
+                           else "headq_decode_attn (decode_split_kernel + decode_reduce_kernel)"),
+                "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                "traffic": traffic,
+                "algorithmic_bytes_per_launch": alg_bytes,
+                "bytes_per_token_kv_head": per_tok,
+                "copy_ceiling_gbs": copy_gbs,
+                "frac_of_copy_ceiling": achieved / copy_gbs,
+            },
+            "decode_ms": float(decode_ms.mean()),
+            "decode_ms_p10_p90": [float(np.percentile(decode_ms, 10)), float(np.percentile(decode_ms, 90))],
+            "append_ms": float(append_ms.mean()),
+            "kv_head_tokens_per_s": w.batch * w.n_kv_heads * n_ctx * n_layers / (ms_per_step / 1e3),
+        })
+    result["calibrate_s_host"] = calib_s
+    result["wall_s_timed"] = wall
+    if not args.no_cpu_baseline and not append_only:
         threads = min(16, os.cpu_count() or 1)
         result["cpu_baseline"] = cpu_baseline(w, U, threads, min(args.cpu_rows, w.batch))
     print(json.dumps(result), flush=True)

@@ -32,15 +32,20 @@
  * Cache format (per layer). Every buffer is indexed [b][h] first (batch, KV head), then by
  * token; `cap` = capacity in tokens (a multiple of 32); G = 32 tokens per group; d = head_dim;
  * r = rank. All buffers must be 16-byte aligned.
- *   kcode  u8   [B][Hkv][cap][d/4]       2-bit base codes; byte c/4 holds channel c at bits 2(c%4)
+ *   kcode  u8   [B][Hkv][cap][d/4]       2-bit base codes, d/16 little-endian 32-bit words per
+ *                                        token: channel 16m + j (j = 8q + 2b + e) at bit
+ *                                        8b + 4e + 2q of word m (one mask or one shift leaves
+ *                                        one code per nibble, in channel order)
  *   kmeta  fp16 [B][Hkv][cap/G][2][d]    per (group, channel): row 0 = step s, row 1 = zero z
  *   scode  u8   [B][Hkv][cap][r/2]       4-bit side codes u = zc + 8; component 2i in the low
  *                                        nibble of byte i, component 2i+1 in the high nibble
  *   ssc    fp16 [B][Hkv][cap]            per-token side step sigma (z_hat = sigma * zc)
  *   v      (dense values) f32 or bf16 [B][Hkv][cap/G][d][G]: within a 32-token group the values
  *                                        are stored channel-major (token index fastest)
- *   vcode  u8   [B][Hkv][cap/G][d][8]    (2-bit values) channel c, group token t = 4b+m at
- *                                        byte b, bits 2m
+ *   vcode  u8   [B][Hkv][cap/G][d*8]     (2-bit values) per group, in matrix-operand order: lane
+ *                                        l = 16*(t/8) + c%16 owns bytes [l*d/8, (l+1)*d/8), two
+ *                                        per 16-channel tile c/16; token item i = t%8 = 4q+2b+e
+ *                                        sits in byte b of that pair at bit 4e + 2q
  *   vmeta  fp16 [B][Hkv][cap/G][2][d/32][G]  (2-bit values) per (token, 32-channel group):
  *                                        row 0 = step, row 1 = zero, token index fastest
  *   U      f32  [Hkv][d][r]              the side basis (device copy of headq_calibrate's output)
@@ -156,7 +161,7 @@ headq_status headq_cache_append(const headq_config* cfg, const headq_cache* cach
  *   corr_scale  multiplies the correction: 1 = HeadQ, 0 = base code only, -1 = wrong sign
  *   logits_dbg  device f32 [B][Hq][n_ctx] corrected logits in natural-log units, or NULL
  *   n_splits    token splits per (b, h); 0 = automatic, else 1..n_ctx/32 (at most 128 with
- *               dense bf16 values)
+ *               dense bf16 or 2-bit values, the matrix-core path)
  *   ws, ws_bytes  device workspace. With ws == NULL the call only stores the bytes it needs in
  *               *ws_bytes and returns HEADQ_OK (nothing is launched). Otherwise *ws_bytes is
  *               the size of ws. The workspace must be zero-filled before its first use; every

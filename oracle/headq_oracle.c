@@ -306,13 +306,17 @@ int orc_quantize_values(int d, int bits, int64_t T, const float* v, uint8_t* cod
 /* ------------------------------------------------------------------------------------------ */
 /* Packing into the cache format (byte layouts are this repository's convention). */
 
+/* Bit position of channel 16m + j inside the 32-bit little-endian word m of a token's key codes:
+ * j = 8q + 2b + e sits in byte b at bit 4e + 2q. */
+static int kcode_bit(int j) { return 8 * ((j % 8) / 2) + 4 * (j % 2) + 2 * (j / 8); }
+
 int orc_pack_kcode(int d, int64_t T, const uint8_t* codes, uint8_t* kcode) {
-  if (d % 4 || !codes || !kcode) return -1;
+  if (d % 16 || !codes || !kcode) return -1;
   for (int64_t t = 0; t < T; ++t)
-    for (int c = 0; c < d; ++c) {
-      uint8_t* byte = &kcode[t * (d / 4) + c / 4];
-      if (c % 4 == 0) *byte = 0;
-      *byte = (uint8_t)(*byte | ((codes[t * d + c] & 3u) << (2 * (c % 4))));
+    for (int m = 0; m < d / 16; ++m) {
+      uint32_t word = 0;
+      for (int j = 0; j < 16; ++j) word |= (uint32_t)(codes[t * d + 16 * m + j] & 3u) << kcode_bit(j);
+      for (int k = 0; k < 4; ++k) kcode[t * (d / 4) + 4 * m + k] = (uint8_t)(word >> (8 * k));
     }
   return 0;
 }
@@ -350,15 +354,27 @@ int orc_pack_vdense(int d, int64_t T, int elem_bytes, const void* v, void* vdens
   return 0;
 }
 
+/* Byte and bit of (channel c, token tt of its group) inside a group's block of value codes:
+ * lane = 16 * (tt / 8) + c % 16 owns d/8 consecutive bytes, two per 16-channel tile c / 16; token
+ * item i = tt % 8 = 4q + 2b + e sits in byte b of the tile's pair at bit 4e + 2q. */
+static int64_t vcode_byte(int d, int c, int tt) {
+  const int lane = 16 * (tt / 8) + c % 16, i = tt % 8;
+  return ((int64_t)lane * (d / 16) + c / 16) * 2 + (i % 4) / 2;
+}
+static int vcode_bit(int tt) {
+  const int i = tt % 8;
+  return 4 * (i % 2) + 2 * (i / 4);
+}
+
 int orc_pack_vcode(int d, int64_t T, const uint8_t* codes, uint8_t* vcode) {
-  if (T % GROUP || !codes || !vcode) return -1;
-  for (int64_t g = 0; g < T / GROUP; ++g)
-    for (int c = 0; c < d; ++c)
-      for (int b = 0; b < 8; ++b) {
-        unsigned byte = 0;
-        for (int m = 0; m < 4; ++m) byte |= (codes[(g * GROUP + 4 * b + m) * d + c] & 3u) << (2 * m);
-        vcode[(g * d + c) * 8 + b] = (uint8_t)byte;
-      }
+  if (T % GROUP || d % 16 || !codes || !vcode) return -1;
+  for (int64_t g = 0; g < T / GROUP; ++g) {
+    uint8_t* blk = vcode + g * d * 8;
+    memset(blk, 0, (size_t)d * 8);
+    for (int tt = 0; tt < GROUP; ++tt)
+      for (int c = 0; c < d; ++c)
+        blk[vcode_byte(d, c, tt)] |= (uint8_t)((codes[(g * GROUP + tt) * d + c] & 3u) << vcode_bit(tt));
+  }
   return 0;
 }
 
@@ -382,7 +398,8 @@ int orc_pack_vmeta(int d, int64_t T, const uint16_t* scale, const uint16_t* zero
  * kappa multiplies the correction (1 = HeadQ, 0 = base only, -1 = the wrong-sign control). */
 
 static double k_hat(const uint8_t* kcode_t, const uint16_t* kmeta_g, int d, int c) {
-  unsigned code = (kcode_t[c / 4] >> (2 * (c % 4))) & 3u;
+  const int m = c / 16, j = c % 16, bit = kcode_bit(j);
+  unsigned code = (kcode_t[4 * m + bit / 8] >> (bit % 8)) & 3u;
   double s = orc_f16_to_f32(kmeta_g[c]);
   double z = orc_f16_to_f32(kmeta_g[d + c]);
   return (double)code * s + z;
@@ -397,7 +414,7 @@ static double v_hat(int value_mode, int value_dtype, const void* vdense, const u
     return orc_bf16_to_f32(((const uint16_t*)vdense)[idx]);
   }
   const int ng = d / GROUP;
-  unsigned code = (vcode[(g * d + c) * 8 + tt / 4] >> (2 * (tt % 4))) & 3u;
+  unsigned code = (vcode[g * d * 8 + vcode_byte(d, c, (int)tt)] >> vcode_bit((int)tt)) & 3u;
   double s = orc_f16_to_f32(vmeta[((g * 2 + 0) * ng + c / GROUP) * GROUP + tt]);
   double z = orc_f16_to_f32(vmeta[((g * 2 + 1) * ng + c / GROUP) * GROUP + tt]);
   return (double)code * s + z;

@@ -59,11 +59,16 @@ int orc_quantize_values(int d, int bits, int64_t T, const float* v, uint8_t* cod
                         uint16_t* zero);
 
 /* Packing into the cache format (one stream; offsets for (b, h) are the caller's).
- *   kcode [T][d/4]: byte c/4 holds channel c at bits 2*(c%4)
+ *   kcode [T][d/4] (d % 16 == 0): d/16 little-endian 32-bit words per token; channel 16m + j with
+ *         j = 8q + 2b + e lies in word m, byte b, bits 4e + 2q (so masking a word with 0x33333333
+ *         leaves channels 16m..16m+7 and the word shifted right by 2 leaves 16m+8..16m+15, two
+ *         channels per byte in ascending order, one per nibble)
  *   kmeta [T/32][2][d]: row 0 = scale, row 1 = zero (fp16)
  *   scode [T][r/2]: byte i/2 holds (zc_i + 8) in the low nibble for even i, high nibble for odd i
  *   vdense [T/32][d][32]: element (token t, channel c) at group t/32, offset c*32 + t%32
- *   vcode [T/32][d][8]: channel c, token t%32 = 4*b + m at byte b, bits 2*m
+ *   vcode [T/32][d*8] (d % 16 == 0): per group, lane l = 16*(t%32 / 8) + c%16 owns bytes
+ *         [l*d/8, (l+1)*d/8), two per 16-channel tile c/16; token item i = t%8 = 4q + 2b + e lies
+ *         in byte b of the tile's pair at bits 4e + 2q
  *   vmeta [T/32][2][d/32][32]: row 0 = scale, row 1 = zero, token-minor */
 int orc_pack_kcode(int d, int64_t T, const uint8_t* codes, uint8_t* kcode);
 int orc_pack_kmeta(int d, int64_t T, const uint16_t* scale, const uint16_t* zero, uint16_t* kmeta);

@@ -156,7 +156,7 @@ def empty_cache(B, Hkv, cap, d, r, value_mode, value_dtype):
         dt = np.float32 if value_dtype == 0 else np.uint16
         c["v"] = np.zeros((B, Hkv, cap // GROUP, d, GROUP), dt)
     else:
-        c["vcode"] = np.zeros((B, Hkv, cap // GROUP, d, 8), np.uint8)
+        c["vcode"] = np.zeros((B, Hkv, cap // GROUP, d * 8), np.uint8)
         c["vmeta"] = np.zeros((B, Hkv, cap // GROUP, 2, d // GROUP, GROUP), np.uint16)
     return c
 
@@ -192,7 +192,7 @@ def write_stream(cache, b, h, start, k, v, U_h, value_mode, value_dtype, bits=2,
             cache["v"][b, h, g0:g1] = dst
         else:
             vq = quantize_values(v, bits)
-            vc = np.zeros((n // GROUP, d, 8), np.uint8)
+            vc = np.zeros((n // GROUP, d * 8), np.uint8)
             _check(L.orc_pack_vcode(d, n, _p(vq["codes"]), _p(vc)), "pack_vcode")
             cache["vcode"][b, h, g0:g1] = vc
             vm = np.zeros((n // GROUP, 2, d // GROUP, GROUP), np.uint16)

@@ -189,7 +189,7 @@ class DeviceCache:
             vdt = torch.float32 if cfg.value_dtype == HEADQ_F32 else torch.bfloat16
             self.v = torch.zeros((B, H, cap // GROUP, d, GROUP), dtype=vdt, device=device)
         else:
-            self.vcode = torch.zeros((B, H, cap // GROUP, d, 8), dtype=u8, device=device)
+            self.vcode = torch.zeros((B, H, cap // GROUP, d * 8), dtype=u8, device=device)
             self.vmeta = torch.zeros((B, H, cap // GROUP, 2, d // GROUP, GROUP), dtype=i16, device=device)
         self.U = None
 

@@ -130,7 +130,7 @@ __global__ __launch_bounds__(kThreads) void append_keys_kernel(AppendArgs a) {
       const int c = c0 + j;
       const float k = ke[t][c];
       const uint32_t code = base_code(k, z_s[c], inv_s[c]);
-      word |= code << (2 * j);
+      word |= code << kcode_bit(j);
       ke[t][c] = k - __builtin_fmaf((float)code, s_s[c], z_s[c]);
     }
     *reinterpret_cast<uint32_t*>(a.kcode + (bh * a.cap + tok0 + t) * (D / 4) + c0 / 4) = word;
@@ -244,15 +244,21 @@ __global__ __launch_bounds__(kThreads) void append_values_q2_kernel(AppendArgs a
     inv_s[t][gc] = inv;
   }
   __syncthreads();
-  // byte (channel c, b) packs tokens 4b..4b+3
+  // Group block of d*8 code bytes in matrix-operand order: lane l = 16*quad + n owns d/8 bytes,
+  // two per 16-channel tile ct (channel 16*ct + n, tokens 8*quad .. 8*quad+7); token item
+  // i = 4q + 2b + e of the eight sits in byte b of the pair at bit 4e + 2q.
   for (int i = threadIdx.x; i < D * 8; i += kThreads) {
-    const int c = i / 8, bb = i % 8, gc = c / 32;
+    const int lane = i / (D / 8), within = i % (D / 8);
+    const int c = 16 * (within / 2) + lane % 16, bb = within % 2, gc = c / 32;
+    const int t0 = 8 * (lane / 16) + 2 * bb;
     uint32_t byte = 0;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int t = 4 * bb + m;
-      byte |= base_code(tile[t][c], z_s[t][gc], inv_s[t][gc]) << (2 * m);
-    }
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int t = t0 + 4 * q + e;
+        byte |= base_code(tile[t][c], z_s[t][gc], inv_s[t][gc]) << (4 * e + 2 * q);
+      }
     a.vcode[g_abs * D * 8 + i] = (uint8_t)byte;
   }
 }

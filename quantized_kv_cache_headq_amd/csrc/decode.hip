@@ -120,7 +120,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
         float acc = 0.0f;
 #pragma unroll
         for (int c = 0; c < D; ++c) {
-          const float code = (float)((words[c / 16] >> (2 * (c % 16))) & 3u);
+          const float code = (float)((words[c / 16] >> kcode_bit(c % 16)) & 3u);
           acc = fmaf(qbar[hh][c], fmaf(code, sz[0][c], sz[1][c]), acc);
         }
         if constexpr (R > 0) {
@@ -192,13 +192,15 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
       } else {
         constexpr int NG = D / 32;
         const int gc = c_own / 32;
-        const uint2 cw = *(const uint2*)(a.vcode + (gabs * D + c_own) * 8);
+        uint32_t cw[4];  // the channel's 16-bit code pairs of tokens 8*qd .. 8*qd+7
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd)
+          cw[qd] = *(const uint16_t*)(a.vcode + gabs * D * 8 + vcode_pair_offset(D, c_own, 8 * qd));
         const uint16_t* vs = a.vmeta + (gabs * 2 + 0) * NG * kGroup + gc * kGroup;
         const uint16_t* vz = a.vmeta + (gabs * 2 + 1) * NG * kGroup + gc * kGroup;
 #pragma unroll
         for (int t = 0; t < kGroup; ++t) {
-          const uint32_t word = t < 16 ? cw.x : cw.y;
-          const float code = (float)((word >> (2 * (t % 16))) & 3u);
+          const float code = (float)((cw[t / 8] >> vcode_pair_bit(t)) & 3u);
           v[t] = fmaf(code, f16_bits_to_f32(vs[t]), f16_bits_to_f32(vz[t]));
         }
       }

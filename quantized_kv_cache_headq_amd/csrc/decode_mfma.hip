@@ -48,6 +48,8 @@ typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -70,20 +72,34 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, kBufferConfig);
 }
 
-// 8 two-bit codes laid out as "code 2p at bit 4p, code 2p+1 at bit 4p+16" -> 8 exact f16
-// values 0..3 (built as the f16 1024 + code, then 1024 subtracted in packed f16).
-__device__ __forceinline__ half8_t codes8_f16(uint32_t y) {
-  u32x4 w;
-  w[0] = (y & 0x00030003u) | 0x64006400u;
-  w[1] = ((y >> 4) & 0x00030003u) | 0x64006400u;
-  w[2] = ((y >> 8) & 0x00030003u) | 0x64006400u;
-  w[3] = ((y >> 12) & 0x00030003u) | 0x64006400u;
-  return bitcast<half8_t>(w) - (half8_t)(_Float16)1024.0f;
+// Two-bit codes to exact f16 / bf16 operands. A packed word masked with 0x33333333 (or shifted
+// right by 2 first) holds one code per nibble; each byte is then one fp4 (e2m1) pair, whose
+// values 0, 0.5, 1, 1.5 scaled by 2 are the codes 0..3 exactly (gfx950 packed fp4 conversion,
+// low nibble to the low half).
+__device__ __forceinline__ uint32_t even_codes(uint32_t w) { return w & 0x33333333u; }
+__device__ __forceinline__ uint32_t odd_codes(uint32_t w) { return (w >> 2) & 0x33333333u; }
+template <int B>
+__device__ __forceinline__ uint32_t fp4_pair_f16(uint32_t m) {
+  return bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(m, 2.0f, B));
 }
-// Rearrange one 32-bit word of packed codes (code j at bits 2j) for codes8_f16: low and high
-// 16-bit halves, each with its odd codes moved up by 14 bits.
-__device__ __forceinline__ uint32_t spread_lo(uint32_t w) { return (w & 0xffffu) | ((w << 14) & 0xffff0000u); }
-__device__ __forceinline__ uint32_t spread_hi(uint32_t w) { return (w >> 16) | ((w >> 2) & 0xffff0000u); }
+template <int B>
+__device__ __forceinline__ uint32_t fp4_pair_bf16(uint32_t m) {
+  return bitcast<uint32_t>(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(m, 2.0f, B));
+}
+// 8 key codes (f16) from a masked word: byte b holds the channel pair (2b, 2b+1) of the run.
+__device__ __forceinline__ half8_t key_codes8(uint32_t m) {
+  const u32x4 w = {fp4_pair_f16<0>(m), fp4_pair_f16<1>(m), fp4_pair_f16<2>(m), fp4_pair_f16<3>(m)};
+  return bitcast<half8_t>(w);
+}
+// 8 value codes (bf16) of one channel tile from a word of the lane's value codes: the low 16 bits
+// are tile 2w, the high 16 bits tile 2w+1; even-masked bytes hold token items 0..3, odd-masked
+// bytes items 4..7.
+template <int HALF>
+__device__ __forceinline__ bf16x8_t value_codes8(uint32_t e, uint32_t o) {
+  const u32x4 w = {fp4_pair_bf16<2 * HALF>(e), fp4_pair_bf16<2 * HALF + 1>(e), fp4_pair_bf16<2 * HALF>(o),
+                   fp4_pair_bf16<2 * HALF + 1>(o)};
+  return bitcast<bf16x8_t>(w);
+}
 
 // 4 offset-binary nibbles (low 16 bits of x, component i at bits 4i) -> 4 exact f16 values u - 8.
 __device__ __forceinline__ half4_t nibbles4_f16(uint32_t x16) {
@@ -131,19 +147,21 @@ __device__ __forceinline__ void lds_wave_fence() {
 
 // Wave-uniform view of one (b, h) stream of the cache.
 struct Stream {
-  __amdgpu_buffer_rsrc_t kcode, kmeta, scode, ssc, v;
+  __amdgpu_buffer_rsrc_t kcode, kmeta, scode, ssc, v, vmeta;
 };
 
-// Key-side bytes of one 32-token group, staged per wave in LDS in this order:
-//   packed codes 32 x d/4 | step/zero rows 2 x d x 2 | side codes 32 x r/2 | sigma 32 x 2.
+// Bytes of one 32-token group staged per wave in LDS, in this order:
+//   packed key codes 32 x d/4 | key step/zero rows 2 x d x 2 | side codes 32 x r/2 |
+//   sigma 32 x 2 | (2-bit values) value step/zero rows 2 x d/32 x 32 x 2.
 // Every array of a group is contiguous in the cache, so each is fetched with one load
 // instruction in which lane L takes bytes [L*w, L*w + w) (w = 16, 8, 4, 2 or 1): fully
 // coalesced, whatever pieces the matrix operands need afterwards.
-template <int D, int R>
+template <int D, int R, bool VQ2>
 struct KSide {
   static constexpr int KC = kGroup * D / 4, KM = 4 * D, SC = kGroup * R / 2, SG = R > 0 ? kGroup * 2 : 0;
-  static constexpr int OFF_KM = KC, OFF_SC = KC + KM, OFF_SG = KC + KM + SC;
-  static constexpr int BYTES = (KC + KM + SC + SG + 15) / 16 * 16;
+  static constexpr int VM = VQ2 ? 4 * D : 0;
+  static constexpr int OFF_KM = KC, OFF_SC = KC + KM, OFF_SG = KC + KM + SC, OFF_VM = KC + KM + SC + SG;
+  static constexpr int BYTES = (KC + KM + SC + SG + VM + 15) / 16 * 16;
 };
 
 template <int N>
@@ -163,33 +181,51 @@ __device__ __forceinline__ typename Bytes<N>::T load_piece(__amdgpu_buffer_rsrc_
   if constexpr (N == 1) return __builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, kStream);
 }
 
+// Word w of a lane's piece (N bytes, N/4 words).
+template <int N>
+__device__ __forceinline__ uint32_t word_of(const typename Bytes<N>::T& x, int w) {
+  if constexpr (N == 4) return x;
+  else return x[w];
+}
+
 // Raw bytes of one 32-token group as one lane holds them (filled one group ahead).
-template <int D, int R>
+template <int D, int R, bool VQ2>
 struct GroupRaw {
   static constexpr int NCT = D / 16;            // channel tiles of the P.V product
-  typename Bytes<D / 8>::T kc;                  // lane's share of the packed codes
-  typename Bytes<D / 16>::T km;                 // lane's share of the step/zero rows
+  typename Bytes<D / 8>::T kc;                  // lane's share of the packed key codes
+  typename Bytes<D / 16>::T km;                 // lane's share of the key step/zero rows
   typename Bytes<(R > 0 ? R / 4 : 1)>::T sc;    // lane's share of the side codes
   uint8_t sg;                                   // lane's share of the sigmas
-  u32x4 v[NCT];                                 // values: channel 16*ct + n, tokens 8*quad .. +7
+  u32x4 v[VQ2 ? 1 : NCT];                       // dense: channel 16*ct + n, tokens 8*quad .. +7
+  typename Bytes<D / 8>::T vc;                  // 2-bit: the lane's value codes (all tiles)
+  typename Bytes<D / 16>::T vm;                 // 2-bit: lane's share of the value step/zero rows
 };
 
-template <int D, int R>
-__device__ __forceinline__ void load_group(GroupRaw<D, R>& g, const Stream& s, int lane, int n, int quad,
-                                           int64_t gi) {
-  constexpr int NCT = D / 16;
-  g.kc = load_piece<D / 8>(s.kcode, lane * (D / 8), (int)(gi * KSide<D, R>::KC));
-  g.km = load_piece<D / 16>(s.kmeta, lane * (D / 16), (int)(gi * KSide<D, R>::KM));
+template <int D, int R, bool VQ2>
+__device__ __forceinline__ void load_group(GroupRaw<D, R, VQ2>& g, const Stream& s, int lane, int n, int quad,
+                                           int gi_in) {
+  using KS = KSide<D, R, VQ2>;
+  // the group index is wave-uniform; saying so keeps every group offset in a scalar register
+  // (a per-lane offset would make the compiler loop over the lanes around each buffer load)
+  const int gi = __builtin_amdgcn_readfirstlane(gi_in);
+  g.kc = load_piece<D / 8>(s.kcode, lane * (D / 8), gi * KS::KC);
+  g.km = load_piece<D / 16>(s.kmeta, lane * (D / 16), gi * KS::KM);
   if constexpr (R > 0) {
-    g.sc = load_piece<R / 4>(s.scode, lane * (R / 4), (int)(gi * KSide<D, R>::SC));
-    g.sg = load_piece<1>(s.ssc, lane, (int)(gi * KSide<D, R>::SG));
+    g.sc = load_piece<R / 4>(s.scode, lane * (R / 4), gi * KS::SC);
+    g.sg = load_piece<1>(s.ssc, lane, gi * KS::SG);
   }
-  const int v0 = (n * kGroup + 8 * quad) * 2;  // channel n (+16*ct), tokens 8*quad .. +7
-  const int v_goff = (int)(gi * (D * kGroup * 2));
+  if constexpr (VQ2) {
+    g.vc = load_piece<D / 8>(s.v, lane * (D / 8), gi * (D * 8));
+    g.vm = load_piece<D / 16>(s.vmeta, lane * (D / 16), gi * (4 * D));
+  } else {
+    constexpr int NCT = D / 16;
+    const int v0 = (n * kGroup + 8 * quad) * 2;  // channel n (+16*ct), tokens 8*quad .. +7
+    const int v_goff = gi * (D * kGroup * 2);
 #pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) {
-    const int off = (ct & 3) * 1024;  // 16 channels x 32 tokens x 2 bytes per tile
-    g.v[ct] = __builtin_amdgcn_raw_buffer_load_b128(s.v, ct < 4 ? v0 : v0 + 4096, v_goff + off, kStream);
+    for (int ct = 0; ct < NCT; ++ct) {
+      const int off = (ct & 3) * 1024;  // 16 channels x 32 tokens x 2 bytes per tile
+      g.v[ct] = __builtin_amdgcn_raw_buffer_load_b128(s.v, ct < 4 ? v0 : v0 + 4096, v_goff + off, kStream);
+    }
   }
 }
 
@@ -204,14 +240,23 @@ struct Fixed {
   float kappa;                     // corr_scale
 };
 
+// x ~ hi + lo in bf16 pairs: hi truncated (the upper half of the f32), lo the remainder rounded
+// to nearest; together ~16 significant bits.
+__device__ __forceinline__ void split_bf16_pair(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  const uint32_t u0 = bitcast<uint32_t>(x0), u1 = bitcast<uint32_t>(x1);
+  hi = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
+  const float2_t r = {x0 - bitcast<float>(u0 & 0xffff0000u), x1 - bitcast<float>(u1 & 0xffff0000u)};
+  lo = bitcast<uint32_t>(__builtin_convertvector(r, bf16x2_t));
+}
+
 // One 32-token group: scores, online-softmax update, P.V accumulation.
-template <int D, int R>
-__device__ __forceinline__ void process_group(const GroupRaw<D, R>& cur, const Fixed<D, R>& f, uint8_t* slot,
-                                              const DecodeArgs& a, int64_t gi, int b, int hq0, int g, int lane, int n,
-                                              int quad, floatx4* o_acc, float& m_run, float& l_run) {
-  constexpr int NKT = D / 32, NCT = D / 16;
-  using KS = KSide<D, R>;
-  // Key side through the wave's LDS slot. Lanes read what other lanes wrote, so the accesses
+template <int D, int R, bool VQ2>
+__device__ __forceinline__ void process_group(const GroupRaw<D, R, VQ2>& cur, const Fixed<D, R>& f, uint8_t* slot,
+                                              const DecodeArgs& a, int gi, int b, int hq0, int g, int lane, int n,
+                                              int quad, floatx4* o_acc, float* z_acc, float& m_run, float& l_run) {
+  constexpr int NKT = D / 32, NCT = D / 16, NG = D / 32;
+  using KS = KSide<D, R, VQ2>;
+  // Staged bytes through the wave's LDS slot. Lanes read what other lanes wrote, so the accesses
   // are ordered by wave-scope fences (the wave executes its LDS operations in order; the fences
   // stop the compiler from moving reads across the writes, in either direction).
   lds_wave_fence();
@@ -221,6 +266,7 @@ __device__ __forceinline__ void process_group(const GroupRaw<D, R>& cur, const F
     *reinterpret_cast<typename Bytes<R / 4>::T*>(slot + KS::OFF_SC + lane * (R / 4)) = cur.sc;
     slot[KS::OFF_SG + lane] = cur.sg;
   }
+  if constexpr (VQ2) *reinterpret_cast<typename Bytes<D / 16>::T*>(slot + KS::OFF_VM + lane * (D / 16)) = cur.vm;
   lds_wave_fence();
   const _Float16* km_h = reinterpret_cast<const _Float16*>(slot + KS::OFF_KM);
   const int row_tok0 = 8 * (n / 4) + (n % 4);  // token of this lane's row in tile 0 (tile 1: +4)
@@ -257,8 +303,10 @@ __device__ __forceinline__ void process_group(const GroupRaw<D, R>& cur, const F
     const half8_t p_lo = __builtin_elementwise_fma(f.bq_lo[t], st[t], e);
 #pragma unroll
     for (int T = 0; T < 2; ++T) {
+      // k-tile t covers channels (d/4)*quad + 8t .. +7: the even (t even) or odd (t odd) run of
+      // the lane's word t/2
       const uint32_t w = kcw[T][(D == 128) ? (t >> 1) : 0];
-      const half8_t ac = codes8_f16((t & 1) ? spread_hi(w) : spread_lo(w));
+      const half8_t ac = key_codes8((t & 1) ? odd_codes(w) : even_codes(w));
       acc[T] = mfma_f16(ac, p_hi, acc[T]);
       acc[T] = mfma_f16(ac, p_lo, acc[T]);
     }
@@ -297,7 +345,7 @@ __device__ __forceinline__ void process_group(const GroupRaw<D, R>& cur, const F
       for (int j = 0; j < 4; ++j) sv[4 * T + j] = f.inv_scale * acc[T][j];
   }
   if (a.logits_dbg && n < g) {
-    float* dst = a.logits_dbg + ((int64_t)b * a.hq + hq0 + n) * a.n_ctx + gi * kGroup + 8 * quad;
+    float* dst = a.logits_dbg + ((int64_t)b * a.hq + hq0 + n) * a.n_ctx + (int64_t)gi * kGroup + 8 * quad;
 #pragma unroll
     for (int j = 0; j < 8; ++j) dst[j] = sv[j] * kLn2;
   }
@@ -311,37 +359,85 @@ __device__ __forceinline__ void process_group(const GroupRaw<D, R>& cur, const F
   const bool grow = mx > m_run + kLazyMax;  // true on the first group (m_run = -inf)
   if (__any(grow)) {
     const float m_new = grow ? mx : m_run;
-    const float alpha = exp2f(m_run - m_new);  // 0 on the first group, 1 if unchanged
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first group, 1 if unchanged
     m_run = m_new;
     l_run *= alpha;
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) o_acc[ct] *= alpha;
+    if constexpr (VQ2)
+#pragma unroll
+      for (int cg = 0; cg < NG; ++cg) z_acc[cg] *= alpha;
   }
-  bf16x8_t p_hi, p_lo;
+  float p[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const float p = exp2f(sv[j] - m_run);
-    l_run += p;
-    const __bf16 ph = (__bf16)p;
-    p_hi[j] = ph;
-    p_lo[j] = (__bf16)(p - (float)ph);
+    p[j] = __builtin_amdgcn_exp2f(sv[j] - m_run);  // v_exp_f32; results below 2^-126 flush to 0
+    l_run += p[j];
   }
+  if constexpr (VQ2) {
+    // v_hat = code * s + z per (token, 32-channel group): the code part is a matrix product with
+    // p o s as the second operand (one per channel group), the zero part sum_j p_j z_j per head
+    // and group is accumulated per lane (tokens 8*quad .. +7) and summed over the quads at the end.
+    const _Float16* vm_h = reinterpret_cast<const _Float16*>(slot + KS::OFF_VM);
+    uint32_t ve[NG], vo[NG];
 #pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) {
-    const bf16x8_t av = bitcast<bf16x8_t>(cur.v[ct]);
-    o_acc[ct] = mfma_bf16(av, p_hi, o_acc[ct]);
-    o_acc[ct] = mfma_bf16(av, p_lo, o_acc[ct]);
+    for (int w = 0; w < NG; ++w) {
+      const uint32_t x = word_of<D / 8>(cur.vc, w);
+      ve[w] = even_codes(x);
+      vo[w] = odd_codes(x);
+    }
+#pragma unroll
+    for (int cg = 0; cg < NG; ++cg) {
+      const half8_t s8 = *reinterpret_cast<const half8_t*>(vm_h + cg * kGroup + 8 * quad);
+      const half8_t z8 = *reinterpret_cast<const half8_t*>(vm_h + (NG + cg) * kGroup + 8 * quad);
+      u32x4 xh, xl;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t h2, l2;
+        // fma with a zero addend maps to one mixed-precision fma (the f16 step read directly)
+        split_bf16_pair(__builtin_fmaf(p[2 * i], (float)s8[2 * i], 0.0f),
+                        __builtin_fmaf(p[2 * i + 1], (float)s8[2 * i + 1], 0.0f), h2, l2);
+        xh[i] = h2;
+        xl[i] = l2;
+      }
+      float za = z_acc[cg];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) za = fmaf(p[j], (float)z8[j], za);
+      z_acc[cg] = za;
+      const bf16x8_t bh = bitcast<bf16x8_t>(xh), bl = bitcast<bf16x8_t>(xl);
+      // tiles 2cg and 2cg+1 = the low and high halves of the lane's code word cg
+      const bf16x8_t a0 = value_codes8<0>(ve[cg], vo[cg]);
+      const bf16x8_t a1 = value_codes8<1>(ve[cg], vo[cg]);
+      o_acc[2 * cg] = mfma_bf16(a0, bh, o_acc[2 * cg]);
+      o_acc[2 * cg] = mfma_bf16(a0, bl, o_acc[2 * cg]);
+      o_acc[2 * cg + 1] = mfma_bf16(a1, bh, o_acc[2 * cg + 1]);
+      o_acc[2 * cg + 1] = mfma_bf16(a1, bl, o_acc[2 * cg + 1]);
+    }
+  } else {
+    bf16x8_t p_hi, p_lo;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const __bf16 ph = (__bf16)p[j];
+      p_hi[j] = ph;
+      p_lo[j] = (__bf16)(p[j] - (float)ph);
+    }
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const bf16x8_t av = bitcast<bf16x8_t>(cur.v[ct]);
+      o_acc[ct] = mfma_bf16(av, p_hi, o_acc[ct]);
+      o_acc[ct] = mfma_bf16(av, p_lo, o_acc[ct]);
+    }
   }
 }
 
-template <int D, int R>
+template <int D, int R, bool VQ2>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_mfma_kernel(DecodeArgs a) {
-  constexpr int NKT = D / 32, NCT = D / 16;
+  constexpr int NKT = D / 32, NCT = D / 16, NG = D / 32;
   constexpr int RU = R > 0 ? R : 1;
   __shared__ float qs[kMaxGqa][D];            // scaled queries
   __shared__ float qu_s[kMaxGqa][RU];         // U^T q (scaled)
   __shared__ float inv_scale_s[kMaxGqa];      // 2^e undoing the per-head query scale
-  __shared__ u32x4 kslot[kWaves][KSide<D, R>::BYTES / 16];  // per-wave key-side staging
+  __shared__ u32x4 kslot[kWaves][KSide<D, R, VQ2>::BYTES / 16];  // per-wave staging of a group
   __shared__ float m_w[kWaves][kMaxGqa], l_w[kWaves][kMaxGqa];
   __shared__ float o_w[kWaves][kMaxGqa][D];
 
@@ -378,20 +474,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // not at the same relative offset together. The first two groups are requested before the
   // prologue so that their latency overlaps it.
   Stream s;
-  const int64_t groups_cap = a.cap / kGroup;
+  const int groups_cap = (int)(a.cap / kGroup);
   s.kcode = make_rsrc(a.kcode + bh * a.cap * (D / 4), a.cap * (D / 4));
-  s.kmeta = make_rsrc(a.kmeta + bh * groups_cap * 2 * D, groups_cap * 4 * D);
+  s.kmeta = make_rsrc(a.kmeta + bh * groups_cap * 2 * D, (int64_t)groups_cap * 4 * D);
   s.scode = make_rsrc(R > 0 ? a.scode + bh * a.cap * (R / 2) : a.kcode, R > 0 ? a.cap * (R / 2) : 0);
   s.ssc = make_rsrc(R > 0 ? a.ssc + bh * a.cap : a.kmeta, R > 0 ? a.cap * 2 : 0);
-  s.v = make_rsrc((const uint16_t*)a.vdense + bh * a.cap * D, a.cap * D * 2);
-  const int64_t n_groups = a.n_ctx / kGroup;
-  const int64_t W = (int64_t)a.n_splits * kWaves;
-  const int64_t rot = (bh * 40503) % n_groups;
-  auto group_at = [&](int64_t j) { const int64_t x = j + rot; return x >= n_groups ? x - n_groups : x; };
-  const int64_t j_begin = (int64_t)split * kWaves + wave;
-  GroupRaw<D, R> ga, gb;  // ping-pong register sets: one group computed while the next loads
-  if (j_begin < n_groups) load_group<D, R>(ga, s, lane, n, quad, group_at(j_begin));
-  if (j_begin + W < n_groups) load_group<D, R>(gb, s, lane, n, quad, group_at(j_begin + W));
+  if constexpr (VQ2) {
+    s.v = make_rsrc(a.vcode + bh * a.cap * (D / 4), a.cap * (D / 4));
+    s.vmeta = make_rsrc(a.vmeta + bh * groups_cap * 2 * D, (int64_t)groups_cap * 4 * D);
+  } else {
+    s.v = make_rsrc((const uint16_t*)a.vdense + bh * a.cap * D, a.cap * D * 2);
+    s.vmeta = s.v;
+  }
+  // group indices are 32-bit and wave-uniform, so every offset below stays in scalar registers
+  const int n_groups = (int)(a.n_ctx / kGroup);
+  const int W = a.n_splits * kWaves;
+  const int rot = (int)((bh * 40503) % n_groups);
+  auto group_at = [&](int j) { const int x = j + rot; return x >= n_groups ? x - n_groups : x; };
+  const int j_begin = split * kWaves + wave;
+  GroupRaw<D, R, VQ2> ga, gb;  // ping-pong register sets: one group computed while the next loads
+  if (j_begin < n_groups) load_group<D, R, VQ2>(ga, s, lane, n, quad, group_at(j_begin));
+  if (j_begin + W < n_groups) load_group<D, R, VQ2>(gb, s, lane, n, quad, group_at(j_begin + W));
   __syncthreads();
 
   // ---- prologue (whole workgroup): per-head power-of-two query scale, U^T q
@@ -450,16 +553,32 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   floatx4 o_acc[NCT];
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) o_acc[ct] = (floatx4){0.f, 0.f, 0.f, 0.f};
+  float z_acc[NG];  // 2-bit values: sum_j p_j z_j per channel group (this lane's tokens)
+#pragma unroll
+  for (int cg = 0; cg < NG; ++cg) z_acc[cg] = 0.0f;
   float m_run = -INFINITY, l_run = 0.0f;
 
   // ---- this wave's groups
   uint8_t* slot = reinterpret_cast<uint8_t*>(kslot[wave]);
-  for (int64_t j = j_begin; j < n_groups; j += 2 * W) {
-    process_group<D, R>(ga, f, slot, a, group_at(j), b, hq0, g, lane, n, quad, o_acc, m_run, l_run);
+  for (int j = j_begin; j < n_groups; j += 2 * W) {
+    process_group<D, R, VQ2>(ga, f, slot, a, group_at(j), b, hq0, g, lane, n, quad, o_acc, z_acc, m_run, l_run);
     if (j + W >= n_groups) break;
-    if (j + 2 * W < n_groups) load_group<D, R>(ga, s, lane, n, quad, group_at(j + 2 * W));
-    process_group<D, R>(gb, f, slot, a, group_at(j + W), b, hq0, g, lane, n, quad, o_acc, m_run, l_run);
-    if (j + 3 * W < n_groups) load_group<D, R>(gb, s, lane, n, quad, group_at(j + 3 * W));
+    if (j + 2 * W < n_groups) load_group<D, R, VQ2>(ga, s, lane, n, quad, group_at(j + 2 * W));
+    process_group<D, R, VQ2>(gb, f, slot, a, group_at(j + W), b, hq0, g, lane, n, quad, o_acc, z_acc, m_run,
+                             l_run);
+    if (j + 3 * W < n_groups) load_group<D, R, VQ2>(gb, s, lane, n, quad, group_at(j + 3 * W));
+  }
+  if constexpr (VQ2) {
+    // zero part of the 2-bit values: sum over the four token quads, added to every channel of
+    // its group (channel 16*ct + 4*quad + j lies in group ct/2)
+#pragma unroll
+    for (int cg = 0; cg < NG; ++cg) {
+      float z = z_acc[cg];
+      z += __shfl_xor(z, 16);
+      z += __shfl_xor(z, 32);
+      o_acc[2 * cg] += z;
+      o_acc[2 * cg + 1] += z;
+    }
   }
 
   // ---- merge the 4 waves of this workgroup, write the split partial
@@ -554,15 +673,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   if (tid == 0) atomicExch(a.ws_count + bh, 0u);
 }
 
-template <int D>
+template <int D, bool VQ2>
 hipError_t launch_r(const DecodeArgs& a, hipStream_t s) {
   dim3 grid((unsigned)a.n_splits, (unsigned)a.hkv, (unsigned)a.batch);
   switch (a.r) {
-    case 0: hipLaunchKernelGGL((decode_mfma_kernel<D, 0>), grid, dim3(kThreads), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((decode_mfma_kernel<D, 4>), grid, dim3(kThreads), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((decode_mfma_kernel<D, 8>), grid, dim3(kThreads), 0, s, a); break;
-    case 16: hipLaunchKernelGGL((decode_mfma_kernel<D, 16>), grid, dim3(kThreads), 0, s, a); break;
-    case 32: hipLaunchKernelGGL((decode_mfma_kernel<D, 32>), grid, dim3(kThreads), 0, s, a); break;
+    case 0: hipLaunchKernelGGL((decode_mfma_kernel<D, 0, VQ2>), grid, dim3(kThreads), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((decode_mfma_kernel<D, 4, VQ2>), grid, dim3(kThreads), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((decode_mfma_kernel<D, 8, VQ2>), grid, dim3(kThreads), 0, s, a); break;
+    case 16: hipLaunchKernelGGL((decode_mfma_kernel<D, 16, VQ2>), grid, dim3(kThreads), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((decode_mfma_kernel<D, 32, VQ2>), grid, dim3(kThreads), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -571,8 +690,9 @@ hipError_t launch_r(const DecodeArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_decode_mfma_split(const DecodeArgs& a, hipStream_t s) {
-  if (a.d == 64) return launch_r<64>(a, s);
-  if (a.d == 128) return launch_r<128>(a, s);
+  const bool q2 = a.value_mode == HEADQ_V_Q2;
+  if (a.d == 64) return q2 ? launch_r<64, true>(a, s) : launch_r<64, false>(a, s);
+  if (a.d == 128) return q2 ? launch_r<128, true>(a, s) : launch_r<128, false>(a, s);
   return hipErrorInvalidValue;
 }
 

@@ -141,14 +141,14 @@ extern "C" headq_status headq_cache_append(const headq_config* cfg, const headq_
 
 namespace {
 
-// The matrix-core kernel handles dense bf16 values; HEADQ_DECODE_KERNEL=valu selects the plain
-// vector kernel instead (kept as the measured comparison and for f32 / 2-bit values).
+// The matrix-core kernel handles dense bf16 values and 2-bit values; HEADQ_DECODE_KERNEL=valu
+// selects the plain vector kernel instead (kept as the measured comparison and for f32 values).
 bool decode_uses_mfma(const headq_config* c) {
   static const bool force_valu = [] {
     const char* s = std::getenv("HEADQ_DECODE_KERNEL");
     return s && std::strcmp(s, "valu") == 0;
   }();
-  return !force_valu && c->value_mode == HEADQ_V_DENSE && c->value_dtype == HEADQ_BF16;
+  return !force_valu && (c->value_mode == HEADQ_V_Q2 || c->value_dtype == HEADQ_BF16);
 }
 
 // Token splits per (b, h) stream: about 2048 waves over the 256 CUs, with every chunk (the

@@ -15,6 +15,19 @@ constexpr int kMaxGqa = 16;    // query heads per KV head supported by the decod
 constexpr int kMaxSplitsMfma = 128;  // splits per stream of the matrix-core decode (its in-kernel
                                      // merge stages 2 * splits * g floats in LDS)
 
+// Packed 2-bit code layouts of the cache (the decode kernels turn a 32-bit word into eight f16 or
+// bf16 operand pairs with one mask, one shift and byte-wise fp4 conversions):
+//   keys   channel 16m + j of a token, j = 8q + 2b + e, at bit 8b + 4e + 2q of 32-bit word m
+//   values per 32-token group, lane l = 16*(t/8) + c%16 owns d/8 bytes, two per 16-channel tile
+//          c/16; token item i = t%8 = 4q + 2b + e sits in byte b of that pair at bit 4e + 2q
+__host__ __device__ constexpr int kcode_bit(int j) { return 8 * ((j % 8) / 2) + 4 * (j % 2) + 2 * (j / 8); }
+__host__ __device__ constexpr int vcode_pair_offset(int d, int c, int t) {  // byte offset of the 16-bit pair
+  return ((16 * ((t % 32) / 8) + c % 16) * (d / 16) + c / 16) * 2;
+}
+__host__ __device__ constexpr int vcode_pair_bit(int t) {  // bit of token t inside its 16-bit pair
+  return 8 * (((t % 8) % 4) / 2) + 4 * (t % 2) + 2 * ((t % 8) / 4);
+}
+
 struct AppendArgs {
   int d, r, hkv, batch;
   int64_t cap;                 // tokens per stream in the cache
@@ -40,7 +53,7 @@ struct DecodeArgs {
   int n_splits;                // token splits (workgroups) per (b, h); one partial result each
   int groups_per_split;        // 32-token groups per chunk; a split has chunks_per_split chunks
   int chunks_per_split;        // 1 (VALU kernel) or 4 (MFMA kernel: one chunk per wave)
-  int use_mfma;                // matrix-core kernel (dense bf16 values)
+  int use_mfma;                // matrix-core kernel (dense bf16 or 2-bit values)
   int query_bf16, value_bf16, value_mode, out_bf16;
   float corr_scale;
   const void* q;

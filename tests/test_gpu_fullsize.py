@@ -16,13 +16,15 @@ from .helpers import oracle_cache
 pytestmark = pytest.mark.gpu
 
 
-def _sampled(wname, streams, out_bf16=False):
+def _sampled(wname, streams, out_bf16=False, batch=None, n_splits=0):
     w = synth.WORKLOADS[wname]
-    say("fullsize", wname, f"B={w.batch} T={w.n_ctx} streams={streams}")
+    if batch is not None:
+        w = synth.scaled(w, batch=batch)
+    say("fullsize", wname, f"B={w.batch} T={w.n_ctx} streams={streams} splits={n_splits or 'auto'}")
     U = orc.calibrate(synth.calibration_queries(w), w.n_kv_heads, w.rank)[0]
     dc, K, V = gpu_cache(w, U)
     q = synth.decode_queries(w)
-    lg, out = decode_gpu(dc, w, q, w.n_ctx, out_bf16=out_bf16)
+    lg, out = decode_gpu(dc, w, q, w.n_ctx, out_bf16=out_bf16, n_splits=n_splits)
     g = w.gqa
     for b, h in streams:
         # oracle cache with a single batch row holding stream (b, h) at KV head h
@@ -59,3 +61,10 @@ def test_qwen7b_decode_full_size_sampled():
 
 def test_tinyllama_decode_full_size_sampled():
     _sampled("tinyllama_decode", [(0, 0), (15, 3)], out_bf16=True)
+
+
+def test_qwen14b_fullkv_full_context_sampled():
+    """Full 32K context of the 2-bit full-KV workload in its benchmark launch shape (one
+    workgroup of four waves per stream: 64 x 8 streams give one split each); the batch is cut to
+    4 rows, which leaves every stream's work unchanged."""
+    _sampled("qwen14b_fullkv", [(0, 0), (3, 7), (2, 5)], out_bf16=True, batch=4, n_splits=1)

@@ -59,6 +59,21 @@ def test_fullkv_two_bit_values_small():
     _case(synth.scaled(W["qwen14b_fullkv"]), 1, 512)
 
 
+def test_fullkv_two_bit_values_d64_ragged_splits():
+    w = synth.scaled(W["tinyllama_decode"], value_mode="q2", batch=2)
+    _case(w, 2, 512, cap=640, n_ctx=416, out_bf16=True, n_splits=3)
+
+
+@pytest.mark.parametrize("rank", [0, 32])
+def test_fullkv_two_bit_values_ranks(rank):
+    _case(synth.scaled(W["qwen14b_fullkv"], n_q_heads=10, n_kv_heads=2, rank=rank), 1, 384, n_splits=2)
+
+
+def test_fullkv_two_bit_values_f32_input_gqa16():
+    w = synth.scaled(W["qwen14b_fullkv"], n_q_heads=32, n_kv_heads=2, value_dtype="f32", key_dtype="f32")
+    _case(w, 1, 256)
+
+
 @pytest.mark.parametrize("rank", [0, 4, 8, 32])
 def test_rank_variants(rank):
     _case(synth.scaled(W["qwen7b_decode"], n_q_heads=8, n_kv_heads=2, rank=rank), 1, 256)

@@ -64,14 +64,31 @@ def test_f32_to_bf16_matches_torch():
     assert np.array_equal(orc.f32_to_bf16_bits(x), ref)
 
 
-def test_kcode_pack_roundtrip_all_patterns():
-    # every byte value as 4 two-bit codes, for 256 tokens x d=4
-    d = 4
-    T = 256
-    codes = np.array([[(t >> (2 * m)) & 3 for m in range(d)] for t in range(T)], np.uint8)
+def test_kcode_pack_every_byte_value_in_every_byte():
+    """Key-code word layout: byte k of a 16-channel word holds channels 2k (bits 0-1), 8+2k (2-3),
+    2k+1 (4-5) and 9+2k (6-7). Every byte value is produced in every byte position."""
+    d, T = 16, 256 * 4
+    codes = np.zeros((T, d), np.uint8)
+    for k in range(4):
+        v = np.arange(256)
+        rows = slice(256 * k, 256 * (k + 1))
+        codes[rows, 2 * k] = v & 3
+        codes[rows, 8 + 2 * k] = (v >> 2) & 3
+        codes[rows, 2 * k + 1] = (v >> 4) & 3
+        codes[rows, 9 + 2 * k] = (v >> 6) & 3
     out = np.zeros((T, d // 4), np.uint8)
     assert orc.lib().orc_pack_kcode(d, T, orc._p(codes), orc._p(out)) == 0
-    assert np.array_equal(out[:, 0], np.arange(256, dtype=np.uint8))
+    for k in range(4):
+        blk = out[256 * k:256 * (k + 1)]
+        assert np.array_equal(blk[:, k], np.arange(256, dtype=np.uint8))
+        assert not np.any(np.delete(blk, k, axis=1))
+    # two words per token at d = 32: the second word holds channels 16..31 the same way
+    codes2 = np.zeros((1, 32), np.uint8)
+    codes2[0, 16 + 9] = 3
+    out2 = np.zeros((1, 8), np.uint8)
+    assert orc.lib().orc_pack_kcode(32, 1, orc._p(codes2), orc._p(out2)) == 0
+    assert list(out2[0]) == [0, 0, 0, 0, 0xC0, 0, 0, 0]
+    assert orc.lib().orc_pack_kcode(4, 1, orc._p(codes2), orc._p(out2)) == -1  # d % 16 != 0
 
 
 def test_scode_pack_roundtrip_all_pairs():
@@ -85,15 +102,25 @@ def test_scode_pack_roundtrip_all_pairs():
 
 
 def test_vcode_and_vdense_layouts_roundtrip():
+    """Value-code group block: lane l = 16*(t/8) + c%16 owns d/8 bytes, two per 16-channel tile;
+    token item i = t%8 = 4q + 2b + e sits in byte b of the tile's pair at bits 4e + 2q."""
     rng = np.random.default_rng(7)
-    T, d = 64, 64
-    codes = rng.integers(0, 4, size=(T, d), dtype=np.uint8)
-    vc = np.zeros((T // 32, d, 8), np.uint8)
-    assert orc.lib().orc_pack_vcode(d, T, orc._p(codes), orc._p(vc)) == 0
-    for t in range(T):
-        for c in range(d):
+    T = 64
+    for d in (64, 128):
+        codes = rng.integers(0, 4, size=(T, d), dtype=np.uint8)
+        vc = np.zeros((T // 32, d * 8), np.uint8)
+        assert orc.lib().orc_pack_vcode(d, T, orc._p(codes), orc._p(vc)) == 0
+        for t in range(T):
             g, tt = divmod(t, 32)
-            assert (vc[g, c, tt // 4] >> (2 * (tt % 4))) & 3 == codes[t, c]
+            i = tt % 8
+            q, b, e = i // 4, (i % 4) // 2, i % 2
+            for c in range(d):
+                lane = 16 * (tt // 8) + c % 16
+                byte = (lane * (d // 16) + c // 16) * 2 + b
+                assert (vc[g, byte] >> (4 * e + 2 * q)) & 3 == codes[t, c]
+        # every code bit is used exactly once
+        assert vc.size * 4 == codes.size
+    d = 64
     v = rng.standard_normal((T, d)).astype(np.float32)
     vd = np.zeros((T // 32, d, 32), np.float32)
     assert orc.lib().orc_pack_vdense(d, T, 4, orc._p(v), orc._p(vd)) == 0
@@ -123,14 +150,17 @@ def test_golden_worked_example_base_quantizer():
     exp_scale = np.array([float(v) for v in g["scale"][0]], np.float32)
     exp_zero = np.array([float(v) for v in g["zero"][0]], np.float32)
     exp_codes = np.array([[int(v) for v in row] for row in g["codes"]], np.uint8)
-    exp_bytes = np.array([int(v, 16) for v in g["kcode_bytes"][0]], np.uint8)
+    exp_words = np.array([int(v, 16) for v in g["kcode_words"][0]], np.uint32)
     enc = orc.encode_keys(keys, None)
     assert np.array_equal(orc.f16_bits_to_f32(enc["scale"][0]), exp_scale)
     assert np.array_equal(orc.f16_bits_to_f32(enc["zero"][0]), exp_zero)
     assert np.array_equal(enc["codes"], exp_codes)
-    kc = np.zeros((32, 1), np.uint8)
-    assert orc.lib().orc_pack_kcode(4, 32, orc._p(enc["codes"]), orc._p(kc)) == 0
-    assert np.array_equal(kc[:, 0], exp_bytes)
+    # packed in a 16-channel word whose channels 4..15 hold code 0
+    codes16 = np.zeros((32, 16), np.uint8)
+    codes16[:, :4] = enc["codes"]
+    kc = np.zeros((32, 4), np.uint8)
+    assert orc.lib().orc_pack_kcode(16, 32, orc._p(codes16), orc._p(kc)) == 0
+    assert np.array_equal(kc.view("<u4")[:, 0], exp_words)
     # residuals of the worked example are exact (dyadic keys)
     exp_resid = np.array([[float(v) for v in row] for row in g["residual"]], np.float32)
     assert np.array_equal(enc["resid"], exp_resid)
