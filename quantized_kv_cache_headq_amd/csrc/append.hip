@@ -4,15 +4,19 @@
 // each key (k_base = B_b(k)), form the residual e = k - k_base, project it on the calibration
 // basis and side-quantize the projection, z = Q_q(U_h^T e); the cache keeps the base code and z.
 //
-// One workgroup (256 threads, 4 wave64) owns one 32-token group of one (b, h) stream:
-//   1. the 32 x d key tile is loaded with 128-bit loads into LDS as f32
-//   2. per channel: min/max over the 32 tokens -> binary16 step s and zero z (kmeta)
+// One launch writes keys and values. A workgroup (256 threads, 4 wave64) owns two 32-token
+// groups of one (b, h) stream (the second one duplicated, with its stores masked, when the
+// token range holds an odd number of groups):
+//   1. both 32 x d key tiles are loaded with 128-bit loads into LDS as f32
+//   2. per (group, channel): min/max over the 32 tokens -> binary16 step s and zero z (kmeta)
 //   3. per (token, 16 channels): 2-bit codes (one 32-bit store) and residuals (back into LDS)
-//   4. per (token, component block): y = U^T e as one sequential f32 fma chain per component
-//      (channel order 0..d-1, the canonical order that makes the side codes reproducible),
-//      then the per-token symmetric 4-bit side quantizer and nibble packing.
-// Values (when given) are written by separate kernels: dense values are transposed into the
-// channel-major group layout, 2-bit values quantized per (token, 32-channel group).
+//   4. projection y = U^T e: wave w owns a run of components and lane l owns token row l of the
+//      64, so U_h is wave-uniform and comes through scalar loads while the residual streams
+//      from LDS; every component is one sequential f32 fma chain over channels 0..d-1 (the
+//      canonical order that makes the side codes reproducible). The per-token maximum |y| is
+//      combined across the waves in LDS; each wave then side-quantizes and packs its components.
+//   5. values (when given): dense values are transposed into the channel-major group layout,
+//      2-bit values quantized per (token, 32-channel group) into the matrix-operand layout.
 //
 // Numerics: no contraction anywhere in this file (every fma is explicit), IEEE division,
 // rint = round half to even, binary16 conversion with round to nearest even.
@@ -26,40 +30,16 @@ namespace headq {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kGpw = 2;               // 32-token groups per workgroup
+constexpr int kRows = kGpw * kGroup;  // token rows per workgroup (one per lane of a wave)
 
-__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+typedef const __attribute__((address_space(4))) float* const_f32_ptr;  // read through scalar loads
 
 __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
   _Float16 h = (_Float16)x;  // v_cvt_f16_f32, round to nearest even
   return __builtin_bit_cast(uint16_t, h);
 }
 __device__ __forceinline__ float f16_bits_to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
-
-// Load a 32 x D tile of f32/bf16 rows (element stride 1 along channels, row stride ts) into an
-// f32 LDS tile with row pitch P.
-template <int D, int P, bool BF16>
-__device__ __forceinline__ void load_tile(float (*dst)[P], const void* src, int64_t ts) {
-  constexpr int kElem = BF16 ? 8 : 4;          // elements per 16-byte load
-  constexpr int kChunks = D / kElem;           // 16-byte chunks per row
-  for (int i = threadIdx.x; i < kGroup * kChunks; i += kThreads) {
-    const int t = i / kChunks, ch = i % kChunks;
-    if constexpr (BF16) {
-      const uint4 w = *reinterpret_cast<const uint4*>((const uint16_t*)src + (int64_t)t * ts + ch * kElem);
-      const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        dst[t][ch * 8 + 2 * j] = __uint_as_float(u[j] << 16);
-        dst[t][ch * 8 + 2 * j + 1] = __uint_as_float(u[j] & 0xffff0000u);
-      }
-    } else {
-      const float4 w = *reinterpret_cast<const float4*>((const float*)src + (int64_t)t * ts + ch * kElem);
-      dst[t][ch * 4 + 0] = w.x;
-      dst[t][ch * 4 + 1] = w.y;
-      dst[t][ch * 4 + 2] = w.z;
-      dst[t][ch * 4 + 3] = w.w;
-    }
-  }
-}
 
 // Min/max grid of one channel (or channel group): compare-select in index order, so that
 // equal values of opposite zero sign resolve the same way as a plain sequential scan.
@@ -79,225 +59,341 @@ __device__ __forceinline__ uint32_t base_code(float k, float z, float inv) {
   return (uint32_t)c;
 }
 
-template <int D, int R, bool KBF16>
-__global__ __launch_bounds__(kThreads) void append_keys_kernel(AppendArgs a) {
-  constexpr int P = D + 4;  // LDS row pitch (floats): spreads token rows over the banks
-  constexpr int RU = R > 0 ? R : 1;
-  __shared__ float ke[kGroup][P];  // keys, then residuals
-  __shared__ float Us[D][RU];
-  __shared__ float s_s[D], z_s[D], inv_s[D];
+// The workgroup's two groups: row = 32 * gl + t. Group gl is group 2 * blockIdx.x + gl of the
+// appended range, clamped to the last one (a duplicate whose stores are masked) when the range
+// holds an odd number of groups. (Plain scalars with selects: a small array indexed by a lane
+// value would live in scratch memory.)
+struct Tile {
+  int64_t bh;
+  int64_t g0, g1;  // range groups of rows 0..31 and 32..63
+  bool v1;         // the second group is real
+  __device__ int64_t g_rel(int gl) const { return gl ? g1 : g0; }
+  __device__ bool valid(int gl) const { return gl ? v1 : true; }
+};
 
-  const int grp = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x;
-  const int64_t bh = (int64_t)b * a.hkv + h;
-  const int64_t tok0 = a.start + (int64_t)grp * kGroup;  // first cache token of this group
+__device__ __forceinline__ Tile tile_of(const AppendArgs& a) {
+  Tile tl;
+  tl.bh = (int64_t)blockIdx.z * a.hkv + blockIdx.y;
+  const int64_t n_groups = a.n_new / kGroup;
+  tl.g0 = (int64_t)blockIdx.x * kGpw;
+  tl.v1 = tl.g0 + 1 < n_groups;
+  tl.g1 = tl.v1 ? tl.g0 + 1 : tl.g0;
+  return tl;
+}
 
-  const char* kin = (const char*)a.k + ((int64_t)b * a.ks_b + (int64_t)h * a.ks_h + (int64_t)grp * kGroup * a.ks_t) *
-                                           (KBF16 ? 2 : 4);
-  load_tile<D, P, KBF16>(ke, kin, a.ks_t);
-  if constexpr (R > 0) {
-    const float* Uh = a.U + (int64_t)h * D * R;
-    for (int i = tid; i < D * R; i += kThreads) Us[i / R][i % R] = Uh[i];
+// Token (within the appended range) of LDS row `row`.
+__device__ __forceinline__ int64_t row_token(const Tile& tl, int row) {
+  return tl.g_rel(row / kGroup) * kGroup + row % kGroup;
+}
+
+// Load the 64 rows of f32/bf16 input (element stride 1 along channels, token stride ts) into an
+// f32 LDS tile with row pitch P, with 128-bit loads.
+template <int D, int P, bool BF16>
+__device__ __forceinline__ void load_rows(float (*dst)[P], const void* base, int64_t ts, const Tile& tl) {
+  constexpr int kElem = BF16 ? 8 : 4;  // elements per 16-byte load
+  constexpr int kChunks = D / kElem;   // 16-byte chunks per row
+  for (int i = threadIdx.x; i < kRows * kChunks; i += kThreads) {
+    const int row = i / kChunks, ch = i % kChunks;
+    const int64_t tok = row_token(tl, row);
+    if constexpr (BF16) {
+      const uint4 w = *reinterpret_cast<const uint4*>((const uint16_t*)base + tok * ts + ch * kElem);
+      const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        dst[row][ch * 8 + 2 * j] = __uint_as_float(u[j] << 16);
+        dst[row][ch * 8 + 2 * j + 1] = __uint_as_float(u[j] & 0xffff0000u);
+      }
+    } else {
+      const float4 w = *reinterpret_cast<const float4*>((const float*)base + tok * ts + ch * kElem);
+      dst[row][ch * 4 + 0] = w.x;
+      dst[row][ch * 4 + 1] = w.y;
+      dst[row][ch * 4 + 2] = w.z;
+      dst[row][ch * 4 + 3] = w.w;
+    }
+  }
+}
+
+// UL: U_h staged in LDS and read with wave-uniform (broadcast) addresses, the shorter critical
+// path for small launches (one group per stream, as in a decode step); otherwise U_h comes
+// through scalar loads, which leaves more LDS for concurrent workgroups of a long prefill.
+template <int D, int R, bool KBF16, bool UL>
+__global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
+  constexpr int P = D + 1;  // LDS row pitch (floats): a column read by 64 rows spreads over the banks
+  // components per wave: r/4, at least 2 so that every wave packs whole bytes (r = 4 uses two waves)
+  constexpr int CW = R / 4 >= 2 ? R / 4 : 2;
+  constexpr int NWP = R > 0 ? R / CW : 0;  // waves that project
+  constexpr int NG = D / 32;               // 32-channel groups (2-bit values)
+  __shared__ float ke[kRows][P];           // keys, then residuals; values in step 5
+  __shared__ float s_s[kGpw * D], z_s[kGpw * D], inv_s[kGpw * D];
+  __shared__ float amax_s[4][kRows];
+  __shared__ float U_s[UL && R > 0 ? D * R : 1];
+
+  const Tile tl = tile_of(a);
+  const int tid = threadIdx.x, lane = tid % 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int64_t groups_cap = a.cap / kGroup;
+  const int64_t g_abs0 = tl.bh * groups_cap + a.start / kGroup;  // cache group of range group 0
+
+  // value rows requested first, into registers: their latency overlaps the whole key pipeline
+  constexpr int VMAX = D / 16;                  // 16-byte chunks per thread for f32 values
+  const bool vbf = a.value_bf16;
+  const int vper = vbf ? 8 : 4;                 // elements per chunk
+  const int vchunks = D / vper;                 // chunks per row
+  const int vpt = kRows * vchunks / kThreads;   // chunks per thread
+  const int64_t vbase = (int64_t)b * a.vs_b + (int64_t)h * a.vs_h;
+  uint4 vr[VMAX];
+  if (a.v) {
+#pragma unroll
+    for (int k = 0; k < VMAX; ++k) {
+      if (k < vpt) {
+        const int i = tid + k * kThreads, row = i / vchunks, c0 = (i % vchunks) * vper;
+        const char* src = (const char*)a.v + (vbase + row_token(tl, row) * a.vs_t + c0) * (vbf ? 2 : 4);
+        vr[k] = *reinterpret_cast<const uint4*>(src);
+      }
+    }
+  }
+
+  const char* kin = (const char*)a.k + ((int64_t)b * a.ks_b + (int64_t)h * a.ks_h) * (KBF16 ? 2 : 4);
+  load_rows<D, P, KBF16>(ke, kin, a.ks_t, tl);
+  if constexpr (UL && R > 0) {
+    const float4* Ug = reinterpret_cast<const float4*>(a.U + (int64_t)h * D * R);
+    for (int i = tid; i < D * R / 4; i += kThreads) reinterpret_cast<float4*>(U_s)[i] = Ug[i];
   }
   __syncthreads();
 
-  // 2. per-channel step and zero (binary16) over the group
-  if (tid < D) {
-    float lo = ke[0][tid], hi = lo;
+  // 2. per (group, channel) step and zero (binary16) over the 32 tokens
+  for (int i = tid; i < kGpw * D; i += kThreads) {
+    const int gl = i / D, c = i % D;
+    float lo = ke[gl * kGroup][c], hi = lo;
     for (int t = 1; t < kGroup; ++t) {
-      const float x = ke[t][tid];
+      const float x = ke[gl * kGroup + t][c];
       lo = x < lo ? x : lo;
       hi = x > hi ? x : hi;
     }
     float s, z, inv;
     uint16_t sb, zb;
     minmax_step_zero(lo, hi, 3.0f, s, z, inv, sb, zb);
-    uint16_t* meta = a.kmeta + (bh * (a.cap / kGroup) + tok0 / kGroup) * 2 * D;
-    meta[tid] = sb;
-    meta[D + tid] = zb;
-    s_s[tid] = s;
-    z_s[tid] = z;
-    inv_s[tid] = inv;
+    if (tl.valid(gl)) {
+      uint16_t* meta = a.kmeta + (g_abs0 + tl.g_rel(gl)) * 2 * D;
+      meta[c] = sb;
+      meta[D + c] = zb;
+    }
+    s_s[i] = s;
+    z_s[i] = z;
+    inv_s[i] = inv;
   }
   __syncthreads();
 
   // 3. codes (16 channels -> one 32-bit word) and residuals e = k - fma(code, s, z)
-  for (int i = tid; i < kGroup * (D / 16); i += kThreads) {
-    const int t = i / (D / 16), c0 = (i % (D / 16)) * 16;
+  for (int i = tid; i < kRows * (D / 16); i += kThreads) {
+    const int row = i / (D / 16), c0 = (i % (D / 16)) * 16, gl = row / kGroup;
     uint32_t word = 0;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const int c = c0 + j;
-      const float k = ke[t][c];
-      const uint32_t code = base_code(k, z_s[c], inv_s[c]);
+      const int c = c0 + j, m = gl * D + c;
+      const float k = ke[row][c];
+      const uint32_t code = base_code(k, z_s[m], inv_s[m]);
       word |= code << kcode_bit(j);
-      ke[t][c] = k - __builtin_fmaf((float)code, s_s[c], z_s[c]);
+      ke[row][c] = k - __builtin_fmaf((float)code, s_s[m], z_s[m]);
     }
-    *reinterpret_cast<uint32_t*>(a.kcode + (bh * a.cap + tok0 + t) * (D / 4) + c0 / 4) = word;
+    if (tl.valid(gl)) {
+      const int64_t tok = a.start + row_token(tl, row);
+      *reinterpret_cast<uint32_t*>(a.kcode + (tl.bh * a.cap + tok) * (D / 4) + c0 / 4) = word;
+    }
   }
 
   if constexpr (R > 0) {
     __syncthreads();
-    // 4. side code: TPT threads per token, CPT consecutive components each
-    constexpr int TPT = (R / 2) < 8 ? (R / 2) : 8;
-    constexpr int CPT = R / TPT;  // 2 or 4
-    const int t = tid / TPT, sub = tid % TPT;
-    if (t < kGroup) {
-      const int i0 = sub * CPT;
-      float y[CPT];
+    // 4. side code. Wave w < NWP projects components [w*CW, (w+1)*CW) of token row `lane`.
+    const int row = lane, gl = row / kGroup;
+    float y[CW];
 #pragma unroll
-      for (int j = 0; j < CPT; ++j) y[j] = 0.0f;
-      for (int c = 0; c < D; c += 4) {
-        const float4 e4 = *reinterpret_cast<const float4*>(&ke[t][c]);
-        const float e[4] = {e4.x, e4.y, e4.z, e4.w};
+    for (int j = 0; j < CW; ++j) y[j] = 0.0f;
+    if (wave < NWP) {
+      if constexpr (UL) {
+        const float* Uw = U_s + wave * CW;
+#pragma unroll 8
+        for (int c = 0; c < D; ++c) {
+          const float e = ke[row][c];
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc)
+          for (int j = 0; j < CW; ++j) y[j] = __builtin_fmaf(Uw[c * R + j], e, y[j]);
+        }
+      } else {
+        const const_f32_ptr Uw = (const_f32_ptr)(a.U + (int64_t)h * D * R) + wave * CW;
+#pragma unroll 8
+        for (int c = 0; c < D; ++c) {
+          const float e = ke[row][c];
 #pragma unroll
-          for (int j = 0; j < CPT; ++j) y[j] = __builtin_fmaf(Us[c + cc][i0 + j], e[cc], y[j]);
+          for (int j = 0; j < CW; ++j) y[j] = __builtin_fmaf(Uw[c * R + j], e, y[j]);
+        }
       }
-      float amax = 0.0f;
+    }
+    float amax = 0.0f;
 #pragma unroll
-      for (int j = 0; j < CPT; ++j) {
-        const float m = __builtin_fabsf(y[j]);
+    for (int j = 0; j < CW; ++j) {
+      const float m = __builtin_fabsf(y[j]);
+      amax = m > amax ? m : amax;
+    }
+    amax_s[wave][row] = amax;
+    __syncthreads();
+    if (wave < NWP) {
+#pragma unroll
+      for (int w = 0; w < NWP; ++w) {
+        const float m = amax_s[w][row];
         amax = m > amax ? m : amax;
-      }
-#pragma unroll
-      for (int off = 1; off < TPT; off <<= 1) {
-        const float o = __shfl_xor(amax, off, TPT);
-        amax = o > amax ? o : amax;
       }
       const uint16_t sg_bits = f32_to_f16_bits(amax / 7.0f);
       const float sg = f16_bits_to_f32(sg_bits);
       const float inv = (sg == 0.0f) ? 0.0f : 1.0f / sg;
       uint32_t packed = 0;
 #pragma unroll
-      for (int j = 0; j < CPT; ++j) {
+      for (int j = 0; j < CW; ++j) {
         float zc = __builtin_rintf(y[j] * inv);
         zc = zc < -7.0f ? -7.0f : zc;
         zc = zc > 7.0f ? 7.0f : zc;
         packed |= (uint32_t)((int)zc + 8) << (4 * j);
       }
-      uint8_t* row = a.scode + (bh * a.cap + tok0 + t) * (R / 2) + i0 / 2;
-      if constexpr (CPT == 4)
-        *reinterpret_cast<uint16_t*>(row) = (uint16_t)packed;
-      else
-        *row = (uint8_t)packed;
-      if (sub == 0) a.ssc[bh * a.cap + tok0 + t] = sg_bits;
-    }
-  }
-}
-
-// Dense values: copy a 32-token group into the channel-major group layout [d][32].
-template <int D, bool VBF16>
-__global__ __launch_bounds__(kThreads) void append_values_dense_kernel(AppendArgs a) {
-  using E = typename std::conditional<VBF16, uint16_t, uint32_t>::type;
-  __shared__ E tile[kGroup][D + (VBF16 ? 2 : 1)];
-  const int grp = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int64_t bh = (int64_t)b * a.hkv + h;
-  const int64_t tok0 = a.start + (int64_t)grp * kGroup;
-  const E* src = (const E*)a.v + (int64_t)b * a.vs_b + (int64_t)h * a.vs_h + (int64_t)grp * kGroup * a.vs_t;
-  for (int i = threadIdx.x; i < kGroup * D; i += kThreads) {
-    const int t = i / D, c = i % D;
-    tile[t][c] = src[(int64_t)t * a.vs_t + c];
-  }
-  __syncthreads();
-  E* dst = (E*)a.vdense + (bh * (a.cap / kGroup) + tok0 / kGroup) * (int64_t)D * kGroup;
-  for (int i = threadIdx.x; i < kGroup * D; i += kThreads) {
-    const int c = i / kGroup, t = i % kGroup;
-    dst[i] = tile[t][c];
-  }
-}
-
-// 2-bit values: per (token, 32-channel group) min/max quantizer, stored channel-major per group.
-template <int D, bool VBF16>
-__global__ __launch_bounds__(kThreads) void append_values_q2_kernel(AppendArgs a) {
-  constexpr int P = D + 1;
-  constexpr int NG = D / 32;
-  __shared__ float tile[kGroup][P];
-  __shared__ float s_s[kGroup][NG], z_s[kGroup][NG], inv_s[kGroup][NG];
-  const int grp = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int64_t bh = (int64_t)b * a.hkv + h;
-  const int64_t tok0 = a.start + (int64_t)grp * kGroup;
-  const int64_t g_abs = bh * (a.cap / kGroup) + tok0 / kGroup;
-  const int64_t base = (int64_t)b * a.vs_b + (int64_t)h * a.vs_h + (int64_t)grp * kGroup * a.vs_t;
-  for (int i = threadIdx.x; i < kGroup * D; i += kThreads) {
-    const int t = i / D, c = i % D;
-    tile[t][c] = VBF16 ? bf16_to_f32(((const uint16_t*)a.v)[base + (int64_t)t * a.vs_t + c])
-                       : ((const float*)a.v)[base + (int64_t)t * a.vs_t + c];
-  }
-  __syncthreads();
-  if (threadIdx.x < kGroup * NG) {
-    const int t = threadIdx.x % kGroup, gc = threadIdx.x / kGroup;
-    float lo = tile[t][gc * 32], hi = lo;
-    for (int c = 1; c < 32; ++c) {
-      const float x = tile[t][gc * 32 + c];
-      lo = x < lo ? x : lo;
-      hi = x > hi ? x : hi;
-    }
-    float s, z, inv;
-    uint16_t sb, zb;
-    minmax_step_zero(lo, hi, 3.0f, s, z, inv, sb, zb);
-    a.vmeta[(g_abs * 2 + 0) * NG * kGroup + gc * kGroup + t] = sb;
-    a.vmeta[(g_abs * 2 + 1) * NG * kGroup + gc * kGroup + t] = zb;
-    s_s[t][gc] = s;
-    z_s[t][gc] = z;
-    inv_s[t][gc] = inv;
-  }
-  __syncthreads();
-  // Group block of d*8 code bytes in matrix-operand order: lane l = 16*quad + n owns d/8 bytes,
-  // two per 16-channel tile ct (channel 16*ct + n, tokens 8*quad .. 8*quad+7); token item
-  // i = 4q + 2b + e of the eight sits in byte b of the pair at bit 4e + 2q.
-  for (int i = threadIdx.x; i < D * 8; i += kThreads) {
-    const int lane = i / (D / 8), within = i % (D / 8);
-    const int c = 16 * (within / 2) + lane % 16, bb = within % 2, gc = c / 32;
-    const int t0 = 8 * (lane / 16) + 2 * bb;
-    uint32_t byte = 0;
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int t = t0 + 4 * q + e;
-        byte |= base_code(tile[t][c], z_s[t][gc], inv_s[t][gc]) << (4 * e + 2 * q);
+      if (tl.valid(gl)) {
+        const int64_t tok = a.start + row_token(tl, row);
+        uint8_t* dst = a.scode + (tl.bh * a.cap + tok) * (R / 2) + wave * (CW / 2);
+        if constexpr (CW == 8)
+          *reinterpret_cast<uint32_t*>(dst) = packed;
+        else if constexpr (CW == 4)
+          *reinterpret_cast<uint16_t*>(dst) = (uint16_t)packed;
+        else
+          *dst = (uint8_t)packed;
+        if (wave == 0) a.ssc[tl.bh * a.cap + tok] = sg_bits;
       }
-    a.vcode[g_abs * D * 8 + i] = (uint8_t)byte;
+    }
+  }
+  if (!a.v) return;
+
+  // 5. values of the same rows (LDS reused once every wave is done with the residuals)
+  __syncthreads();
+  if (a.value_mode == HEADQ_V_DENSE) {
+    // raw elements into LDS, then each group written channel-major ([d][32])
+    uint32_t (*raw)[P] = reinterpret_cast<uint32_t (*)[P]>(ke);
+#pragma unroll
+    for (int k = 0; k < VMAX; ++k) {
+      if (k < vpt) {
+        const int i = tid + k * kThreads, row = i / vchunks, c0 = (i % vchunks) * vper;
+        const uint32_t u[4] = {vr[k].x, vr[k].y, vr[k].z, vr[k].w};
+        if (vbf) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            raw[row][c0 + 2 * j] = u[j] & 0xffffu;
+            raw[row][c0 + 2 * j + 1] = u[j] >> 16;
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) raw[row][c0 + j] = u[j];
+        }
+      }
+    }
+    __syncthreads();
+    for (int i = tid; i < kRows * D; i += kThreads) {
+      const int gl = i / (D * kGroup), c = (i / kGroup) % D, t = i % kGroup;
+      if (!tl.valid(gl)) continue;
+      const int64_t idx = ((g_abs0 + tl.g_rel(gl)) * D + c) * kGroup + t;
+      const uint32_t x = raw[gl * kGroup + t][c];
+      if (vbf)
+        ((uint16_t*)a.vdense)[idx] = (uint16_t)x;
+      else
+        ((uint32_t*)a.vdense)[idx] = x;
+    }
+  } else {
+    // 2-bit values: per (token, 32-channel group) min/max grid, codes in matrix-operand order
+#pragma unroll
+    for (int k = 0; k < VMAX; ++k) {
+      if (k < vpt) {
+        const int i = tid + k * kThreads, row = i / vchunks, c0 = (i % vchunks) * vper;
+        const uint32_t u[4] = {vr[k].x, vr[k].y, vr[k].z, vr[k].w};
+        if (vbf) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            ke[row][c0 + 2 * j] = __uint_as_float(u[j] << 16);
+            ke[row][c0 + 2 * j + 1] = __uint_as_float(u[j] & 0xffff0000u);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) ke[row][c0 + j] = __uint_as_float(u[j]);
+        }
+      }
+    }
+    __syncthreads();
+    // grid of (row, channel group) in the key step/zero arrays, now free: kRows * NG = kGpw * D
+    for (int i = tid; i < kRows * NG; i += kThreads) {
+      const int row = i % kRows, gc = i / kRows, gl = row / kGroup, t = row % kGroup;
+      float lo = ke[row][gc * 32], hi = lo;
+      for (int c = 1; c < 32; ++c) {
+        const float x = ke[row][gc * 32 + c];
+        lo = x < lo ? x : lo;
+        hi = x > hi ? x : hi;
+      }
+      float s, z, inv;
+      uint16_t sb, zb;
+      minmax_step_zero(lo, hi, 3.0f, s, z, inv, sb, zb);
+      if (tl.valid(gl)) {
+        const int64_t gabs = g_abs0 + tl.g_rel(gl);
+        a.vmeta[(gabs * 2 + 0) * NG * kGroup + gc * kGroup + t] = sb;
+        a.vmeta[(gabs * 2 + 1) * NG * kGroup + gc * kGroup + t] = zb;
+      }
+      s_s[row * NG + gc] = s;
+      z_s[row * NG + gc] = z;
+      inv_s[row * NG + gc] = inv;
+    }
+    __syncthreads();
+    // group block of d*8 code bytes: lane l = 16*quad + n owns d/8 bytes, two per 16-channel
+    // tile ct (channel 16*ct + n, tokens 8*quad .. 8*quad+7); token item i = 4q + 2b + e of the
+    // eight sits in byte b of the pair at bit 4e + 2q
+    for (int i = tid; i < kGpw * D * 8; i += kThreads) {
+      const int gl = i / (D * 8), byte = i % (D * 8);
+      const int ln = byte / (D / 8), within = byte % (D / 8);
+      const int c = 16 * (within / 2) + ln % 16, bb = within % 2, gc = c / 32;
+      const int t0 = 8 * (ln / 16) + 2 * bb;
+      uint32_t v = 0;
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int row = gl * kGroup + t0 + 4 * q + e;
+          v |= base_code(ke[row][c], z_s[row * NG + gc], inv_s[row * NG + gc]) << (4 * e + 2 * q);
+        }
+      if (tl.valid(gl)) a.vcode[(g_abs0 + tl.g_rel(gl)) * D * 8 + byte] = (uint8_t)v;
+    }
   }
 }
 
 template <int D, int R>
-hipError_t launch_keys(const AppendArgs& a, hipStream_t s) {
-  dim3 grid((unsigned)(a.n_new / kGroup), (unsigned)a.hkv, (unsigned)a.batch);
-  if (a.key_bf16)
-    hipLaunchKernelGGL((append_keys_kernel<D, R, true>), grid, dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((append_keys_kernel<D, R, false>), grid, dim3(kThreads), 0, s, a);
+hipError_t launch_dr(const AppendArgs& a, hipStream_t s) {
+  const int64_t n_groups = a.n_new / kGroup;
+  dim3 grid((unsigned)((n_groups + kGpw - 1) / kGpw), (unsigned)a.hkv, (unsigned)a.batch);
+  const bool small = (int64_t)grid.x * grid.y * grid.z <= 1024;  // at most ~4 workgroups per CU
+  if (a.key_bf16) {
+    if (small)
+      hipLaunchKernelGGL((append_kernel<D, R, true, true>), grid, dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((append_kernel<D, R, true, false>), grid, dim3(kThreads), 0, s, a);
+  } else {
+    if (small)
+      hipLaunchKernelGGL((append_kernel<D, R, false, true>), grid, dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((append_kernel<D, R, false, false>), grid, dim3(kThreads), 0, s, a);
+  }
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_d(const AppendArgs& a, hipStream_t s) {
-  hipError_t e;
   switch (a.r) {
-    case 0: e = launch_keys<D, 0>(a, s); break;
-    case 4: e = launch_keys<D, 4>(a, s); break;
-    case 8: e = launch_keys<D, 8>(a, s); break;
-    case 16: e = launch_keys<D, 16>(a, s); break;
-    case 32: e = launch_keys<D, 32>(a, s); break;
+    case 0: return launch_dr<D, 0>(a, s);
+    case 4: return launch_dr<D, 4>(a, s);
+    case 8: return launch_dr<D, 8>(a, s);
+    case 16: return launch_dr<D, 16>(a, s);
+    case 32: return launch_dr<D, 32>(a, s);
     default: return hipErrorInvalidValue;
   }
-  if (e != hipSuccess || !a.v) return e;
-  dim3 grid((unsigned)(a.n_new / kGroup), (unsigned)a.hkv, (unsigned)a.batch);
-  if (a.value_mode == HEADQ_V_DENSE) {
-    if (a.value_bf16)
-      hipLaunchKernelGGL((append_values_dense_kernel<D, true>), grid, dim3(kThreads), 0, s, a);
-    else
-      hipLaunchKernelGGL((append_values_dense_kernel<D, false>), grid, dim3(kThreads), 0, s, a);
-  } else {
-    if (a.value_bf16)
-      hipLaunchKernelGGL((append_values_q2_kernel<D, true>), grid, dim3(kThreads), 0, s, a);
-    else
-      hipLaunchKernelGGL((append_values_q2_kernel<D, false>), grid, dim3(kThreads), 0, s, a);
-  }
-  return hipGetLastError();
 }
 
 }  // namespace
