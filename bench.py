@@ -28,8 +28,14 @@ HBM_PEAK_GBS = 8000.0
 FP32_VECTOR_PEAK_TFLOPS = 157.3     # 256 CU x 64 lanes x 2 (packed pair) x 2 flop per fma x 2.4 GHz
 FP32_NONPACKED_PEAK_TFLOPS = 78.6   # the same without packed-fp32 instructions
 METRIC = "decode-attn cached tokens·heads/s + achieved HBM GB/s (% of peak), 1 GPU"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_qwen7b_traffic.json")
-DECODE_SRC = os.path.join(ROOT, "quantized_kv_cache_headq_amd", "csrc", "decode_mfma.hip")
+CSRC = os.path.join(ROOT, "quantized_kv_cache_headq_amd", "csrc")
+# committed rocprofv3 counter summaries per workload: (file, source of the kernel they measured)
+TRAFFIC = {
+    "qwen7b_decode": ("decode_qwen7b_traffic.json", "decode_mfma.hip"),
+    "qwen14b_fullkv": ("decode_qwen14b_fullkv_traffic.json", "decode_mfma.hip"),
+    "tinyllama_decode": ("decode_tinyllama_traffic.json", "decode_mfma.hip"),
+    "append_prefill": ("append_prefill_traffic.json", "append.hip"),
+}
 
 
 def algorithmic_bytes_per_token_head(w) -> int:
@@ -67,18 +73,21 @@ def copy_ceiling(torch, dev, stream) -> float:
     return gbs
 
 
-def source_sha() -> str:
-    return hashlib.sha256(open(DECODE_SRC, "rb").read()).hexdigest()[:16]
+def source_sha(src: str) -> str:
+    return hashlib.sha256(open(os.path.join(CSRC, src), "rb").read()).hexdigest()[:16]
 
 
-def traffic_per_launch():
-    """HBM bytes per decode launch from the committed rocprofv3 counter summary, or None when the
-    decode kernel source changed since the counters were taken."""
+def traffic_per_launch(workload: str):
+    """HBM bytes per launch of the workload's dominant kernel from the committed rocprofv3 counter
+    summary, or None when there is none or the kernel's source changed since it was taken."""
+    if workload not in TRAFFIC:
+        return None
+    fname, src = TRAFFIC[workload]
     try:
-        t = json.load(open(TRAFFIC_FILE))
+        t = json.load(open(os.path.join(ROOT, "profiles", fname)))
     except (OSError, ValueError):
         return None
-    if t.get("source_sha") != source_sha():
+    if t.get("source_sha") != source_sha(src):
         return None
     return t.get("bytes_per_launch")
 
@@ -291,7 +300,7 @@ def main():
             "roofline": {
                 "bound": "alu", "kernel": "append_keys_kernel (one launch)",
                 "achieved": achieved, "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / FP32_VECTOR_PEAK_TFLOPS, "traffic": None,
+                "frac": achieved / FP32_VECTOR_PEAK_TFLOPS, "traffic": traffic_per_launch(w.name),
                 "peak_nonpacked": FP32_NONPACKED_PEAK_TFLOPS,
                 "frac_nonpacked": achieved / FP32_NONPACKED_PEAK_TFLOPS,
                 "algorithmic_flops_per_launch": flops,
@@ -304,8 +313,8 @@ def main():
         alg_bytes = per_tok * w.batch * w.n_kv_heads * n_ctx
         dec_s = float(decode_ms.mean()) / 1e3
         achieved = alg_bytes / dec_s / 1e9
-        mfma = w.value_mode == "dense" and w.value_dtype == "bf16"
-        traffic = traffic_per_launch() if w.name == "qwen7b_decode" else None
+        mfma = w.value_mode == "q2" or w.value_dtype == "bf16"
+        traffic = traffic_per_launch(w.name)
         result.update({
             "value": tok_heads / (ms_per_step / 1e3),
             "unit": "query-head cached tokens/s",
