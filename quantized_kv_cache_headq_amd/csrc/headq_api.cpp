@@ -151,12 +151,13 @@ bool decode_uses_mfma(const headq_config* c) {
   return !force_valu && (c->value_mode == HEADQ_V_Q2 || c->value_dtype == HEADQ_BF16);
 }
 
-// Token splits per (b, h) stream: about 2048 waves over the 256 CUs, with every chunk (the
-// groups one wave walks) at least 4 groups long so the partials stay a small fraction of the
-// traffic.
-int auto_splits(const headq_config* c, int64_t n_groups, int chunks) {
+// Token splits per (b, h) stream. The matrix-core kernel aims at one wave per SIMD (1024 waves
+// over the 256 CUs: measured faster than two, which contend for the same issue slots and memory
+// queues), the vector kernel at two; every chunk (the groups one wave walks) stays at least 4
+// groups long so the partials remain a small fraction of the traffic.
+int auto_splits(const headq_config* c, int64_t n_groups, int chunks, bool mfma) {
   const int64_t streams = (int64_t)c->batch * c->n_kv_heads;
-  const int64_t target_waves = 2048;
+  const int64_t target_waves = mfma ? 1024 : 2048;
   int64_t s = (target_waves + streams * chunks - 1) / (streams * chunks);
   const int64_t min_groups_per_chunk = 4;
   if (s * chunks * min_groups_per_chunk > n_groups) s = n_groups / (chunks * min_groups_per_chunk);
@@ -182,7 +183,7 @@ extern "C" headq_status headq_decode_attn(const headq_config* cfg, const headq_c
   if (n_splits < 0 || n_splits > n_groups) return HEADQ_ERR_SHAPE;
   const bool mfma = decode_uses_mfma(cfg);
   const int chunks = mfma ? 4 : 1;
-  const int S = n_splits ? n_splits : auto_splits(cfg, n_groups, chunks);
+  const int S = n_splits ? n_splits : auto_splits(cfg, n_groups, chunks, mfma);
   if (mfma && S > headq::kMaxSplitsMfma) return HEADQ_ERR_UNSUPPORTED;
   const size_t need = headq::decode_ws_bytes(cfg->batch, cfg->n_q_heads, cfg->n_kv_heads, cfg->head_dim, S);
   if (!ws) {
