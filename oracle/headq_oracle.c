@@ -420,14 +420,23 @@ static double v_hat(int value_mode, int value_dtype, const void* vdense, const u
   return (double)code * s + z;
 }
 
+/* An element of a dense tail row (f32, or bfloat16 bits when dtype == 1). */
+static double tail_at(const void* tail, int dtype, int64_t idx) {
+  if (dtype == 0) return ((const float*)tail)[idx];
+  return orc_bf16_to_f32(((const uint16_t*)tail)[idx]);
+}
+
 int orc_decode(int d, int hq, int hkv, int r, int value_mode, int value_dtype, int B, int64_t cap,
                int64_t n_ctx, const uint8_t* kcode, const uint16_t* kmeta, const uint8_t* scode,
                const uint16_t* ssc, const void* vdense, const uint8_t* vcode, const uint16_t* vmeta,
-               const float* U, const float* q, double kappa, int b_begin, int b_end, double* logits,
-               double* out) {
+               int key_dtype, const void* ktail, const void* vtail, const float* U, const float* q, double kappa,
+               int b_begin, int b_end, double* logits, double* out) {
   if (d <= 0 || d % 4 || hq <= 0 || hkv <= 0 || hq % hkv || r < 0 || r % 2 || cap % GROUP || n_ctx <= 0 ||
       n_ctx > cap || b_begin < 0 || b_end > B || b_begin > b_end || !kcode || !kmeta || !q || !out)
     return -1;
+  /* tokens past the last whole group are the stream's dense tail: exact keys and values */
+  const int64_t n_full = n_ctx / GROUP * GROUP;
+  if (n_full < n_ctx && (!ktail || !vtail)) return -1;
   if (r && (!scode || !ssc || !U)) return -1;
   if (value_mode == 0 && !vdense) return -1;
   if (value_mode == 1 && (!vcode || !vmeta || d % GROUP)) return -1;
@@ -450,7 +459,13 @@ int orc_decode(int d, int hq, int hkv, int r, int value_mode, int value_dtype, i
         qu[i] = acc;
       }
       double smax = -INFINITY;
-      for (int64_t j = 0; j < n_ctx; ++j) {
+      for (int64_t j = n_full; j < n_ctx; ++j) {
+        double dot = 0.0;
+        for (int c = 0; c < d; ++c) dot += qd[c] * tail_at(ktail, key_dtype, (bh * GROUP + j % GROUP) * d + c);
+        s[j] = dot * inv_sqrt_d;
+        if (s[j] > smax) smax = s[j];
+      }
+      for (int64_t j = 0; j < n_full; ++j) {
         const uint8_t* kt = kcode + (bh * cap + j) * (d / 4);
         const uint16_t* mg = kmeta + (bh * (cap / GROUP) + j / GROUP) * 2 * d;
         double base = 0.0;
@@ -477,7 +492,10 @@ int orc_decode(int d, int hq, int hkv, int r, int value_mode, int value_dtype, i
       for (int c = 0; c < d; ++c) o[c] = 0.0;
       for (int64_t j = 0; j < n_ctx; ++j) {
         double p = exp(s[j] - smax) / l;
-        for (int c = 0; c < d; ++c) o[c] += p * v_hat(value_mode, value_dtype, vd, vc, vm, d, j, c);
+        if (j >= n_full)
+          for (int c = 0; c < d; ++c) o[c] += p * tail_at(vtail, value_dtype, (bh * GROUP + j % GROUP) * d + c);
+        else
+          for (int c = 0; c < d; ++c) o[c] += p * v_hat(value_mode, value_dtype, vd, vc, vm, d, j, c);
       }
       for (int c = 0; c < d; ++c) out[((int64_t)b * hq + a) * d + c] = o[c];
       if (logits)

@@ -82,12 +82,15 @@ int orc_pack_vmeta(int d, int64_t T, const uint16_t* scale, const uint16_t* zero
  *   value_mode 0 = dense (value_dtype 0 = f32, 1 = bf16), 1 = 2-bit (vcode/vmeta)
  *   q: f32 [B][hq][d]  U: f32 [hkv][d][r]
  *   logits: f64 [B][hq][n_ctx] natural-log units (nullable)   out: f64 [B][hq][d]
- * Cache buffers are laid out [B][hkv][cap ...] as in the packing comments above. */
+ * Cache buffers are laid out [B][hkv][cap ...] as in the packing comments above. Tokens past the
+ * last whole group (n_ctx % 32 of them) come from the dense tails ktail / vtail [B][hkv][32][d]
+ * (row t % 32; f32, or bfloat16 bits when the dtype is 1) with exact keys and values: no base
+ * code, no side code. The tails may be NULL when n_ctx is a multiple of 32. */
 int orc_decode(int d, int hq, int hkv, int r, int value_mode, int value_dtype, int B, int64_t cap,
                int64_t n_ctx, const uint8_t* kcode, const uint16_t* kmeta, const uint8_t* scode,
                const uint16_t* ssc, const void* vdense, const uint8_t* vcode, const uint16_t* vmeta,
-               const float* U, const float* q, double kappa, int b_begin, int b_end, double* logits,
-               double* out);
+               int key_dtype, const void* ktail, const void* vtail, const float* U, const float* q, double kappa,
+               int b_begin, int b_end, double* logits, double* out);
 
 #ifdef __cplusplus
 }

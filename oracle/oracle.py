@@ -58,7 +58,7 @@ def lib():
         L.orc_pack_vdense.argtypes = [I, I64, I, P, P]
         L.orc_pack_vcode.argtypes = [I, I64, P, P]
         L.orc_pack_vmeta.argtypes = [I, I64, P, P, P]
-        L.orc_decode.argtypes = [I, I, I, I, I, I, I, I64, I64, P, P, P, P, P, P, P, P, P, D, I, I, P, P]
+        L.orc_decode.argtypes = [I, I, I, I, I, I, I, I64, I64, P, P, P, P, P, P, P, I, P, P, P, P, D, I, I, P, P]
         _lib = L
     return _lib
 
@@ -144,8 +144,10 @@ def quantize_values(v, bits: int = 2):
     return dict(codes=codes, scale=scale, zero=zero)
 
 
-def empty_cache(B, Hkv, cap, d, r, value_mode, value_dtype):
-    """Zero-filled buffers of the cache format (numpy, host)."""
+def empty_cache(B, Hkv, cap, d, r, value_mode, value_dtype, key_dtype=None):
+    """Zero-filled buffers of the cache format (numpy, host). With key_dtype given, the dense tails
+    of the unfinished last group are included: ktail / vtail [B][Hkv][32][d] in the key / value
+    dtype (f32, or bfloat16 bit patterns)."""
     c = dict(
         kcode=np.zeros((B, Hkv, cap, d // 4), np.uint8),
         kmeta=np.zeros((B, Hkv, cap // GROUP, 2, d), np.uint16),
@@ -158,15 +160,63 @@ def empty_cache(B, Hkv, cap, d, r, value_mode, value_dtype):
     else:
         c["vcode"] = np.zeros((B, Hkv, cap // GROUP, d * 8), np.uint8)
         c["vmeta"] = np.zeros((B, Hkv, cap // GROUP, 2, d // GROUP, GROUP), np.uint16)
+    if key_dtype is not None:
+        c["ktail"] = np.zeros((B, Hkv, GROUP, d), np.float32 if key_dtype == 0 else np.uint16)
+        c["vtail"] = np.zeros((B, Hkv, GROUP, d), np.float32 if value_dtype == 0 else np.uint16)
     return c
 
 
+def _to_tail(x_f32_or_bits, tail):
+    """Rows for a dense tail: f32 tails take f32 values, bf16 tails bit patterns (uint16)."""
+    if tail.dtype == np.float32:
+        return np.asarray(x_f32_or_bits, np.float32)
+    x = np.asarray(x_f32_or_bits)
+    return x if x.dtype == np.uint16 else f32_to_bf16_bits(x)
+
+
+def _from_tail(rows, as_bits):
+    """Tail rows back as f32 values, or as bf16 bit patterns when as_bits."""
+    if rows.dtype == np.float32:
+        return rows.copy()
+    return rows.copy() if as_bits else bf16_bits_to_f32(rows)
+
+
 def write_stream(cache, b, h, start, k, v, U_h, value_mode, value_dtype, bits=2, side_bits=4):
-    """Encode keys (and values) of one (b, h) stream into `cache` at token offset `start`.
+    """Append tokens [start, start + n) of one (b, h) stream (the cache write of the summary's §3
+    step 2, one token at a time or in any run). Every group that is whole once these tokens are in
+    is encoded; the tokens of an unfinished last group are kept exactly in the dense tails. Tokens
+    of the first group that precede `start` must already be in the tail (earlier appends).
 
     k: f32 [n][d] keys (exact widening of the stored key dtype)
     v: [n][d] values (f32 array for dtype 0, bf16 bit patterns uint16 for dtype 1, f32 for 2-bit)
-    Returns the unpacked encode result for inspection."""
+    Returns the unpacked encode result of the whole groups (None if there are none)."""
+    n, d = k.shape
+    if start % GROUP == 0 and n % GROUP == 0:
+        return _write_groups(cache, b, h, start, k, v, U_h, value_mode, value_dtype, bits, side_bits)
+    g0 = start // GROUP
+    head = start - g0 * GROUP
+    kt, vt = cache["ktail"][b, h], cache["vtail"][b, h]
+    v_bits = v is not None and value_mode == 0 and value_dtype == 1
+    k_all = np.concatenate([_from_tail(kt[:head], False), np.asarray(k, np.float32)])
+    v_all = None
+    if v is not None:
+        v_all = np.concatenate([_from_tail(vt[:head], v_bits), np.asarray(v, np.uint16 if v_bits else np.float32)])
+    n_whole = (start + n) // GROUP - g0
+    enc = None
+    if n_whole > 0:
+        m = n_whole * GROUP
+        enc = _write_groups(cache, b, h, g0 * GROUP, k_all[:m], None if v_all is None else v_all[:m], U_h,
+                            value_mode, value_dtype, bits, side_bits)
+    rest = len(k_all) - n_whole * GROUP
+    if rest:
+        kt[:rest] = _to_tail(k_all[n_whole * GROUP:], kt)
+        if v_all is not None:
+            vt[:rest] = _to_tail(v_all[n_whole * GROUP:], vt)
+    return enc
+
+
+def _write_groups(cache, b, h, start, k, v, U_h, value_mode, value_dtype, bits, side_bits):
+    """Encode whole groups (start and n multiples of 32) into the packed arrays."""
     n, d = k.shape
     r = 0 if U_h is None else U_h.shape[1]
     enc = encode_keys(k, U_h, bits, side_bits)
@@ -216,8 +266,11 @@ def decode(cache, q, U, n_ctx, kappa=1.0, value_mode=0, value_dtype=1, b_range=N
     logits = np.zeros((B, Hq, n_ctx), np.float64) if want_logits else None
     arrs = {k: np.ascontiguousarray(val) for k, val in cache.items()}
     Uc = None if U is None else np.ascontiguousarray(U, dtype=np.float32)
+    kt = arrs.get("ktail")
+    key_dtype = 0 if kt is None or kt.dtype == np.float32 else 1
     _check(lib().orc_decode(d, Hq, Hkv, r, value_mode, value_dtype, B, cap, n_ctx, _p(arrs["kcode"]),
                             _p(arrs["kmeta"]), _p(arrs["scode"]) if r else None, _p(arrs["ssc"]) if r else None,
-                            _p(arrs.get("v")), _p(arrs.get("vcode")), _p(arrs.get("vmeta")), _p(Uc), _p(q),
-                            float(kappa), b0, b1, _p(logits), _p(out)), "decode")
+                            _p(arrs.get("v")), _p(arrs.get("vcode")), _p(arrs.get("vmeta")), key_dtype, _p(kt),
+                            _p(arrs.get("vtail")), _p(Uc), _p(q), float(kappa), b0, b1, _p(logits), _p(out)),
+           "decode")
     return logits, out
