@@ -48,6 +48,8 @@
  *                                        sits in byte b of that pair at bit 4e + 2q
  *   vmeta  fp16 [B][Hkv][cap/G][2][d/32][G]  (2-bit values) per (token, 32-channel group):
  *                                        row 0 = step, row 1 = zero, token index fastest
+ *   ktail  key_dtype   [B][Hkv][G][d]    tokens of the unfinished last group (row t % 32), exact
+ *   vtail  value_dtype [B][Hkv][G][d]    their values, exact (also in 2-bit mode)
  *   U      f32  [Hkv][d][r]              the side basis (device copy of headq_calibrate's output)
  */
 #ifndef HEADQ_H
@@ -105,6 +107,8 @@ typedef struct headq_cache { /* device pointers, layouts in the header comment a
   uint8_t* vcode;  /* 2-bit values (value_mode == HEADQ_V_Q2) */
   uint16_t* vmeta; /* 2-bit values (value_mode == HEADQ_V_Q2) */
   const float* U;  /* [Hkv][d][r]; may be NULL when rank == 0 */
+  void* ktail;     /* dense tail keys; may be NULL if every append and n_ctx is group-aligned */
+  void* vtail;     /* dense tail values; may be NULL likewise */
 } headq_cache;
 
 /*
@@ -135,14 +139,19 @@ headq_status headq_calibrate(const headq_config* cfg, const float* q_cal, int64_
  *   y_i = sum_c U[c][i] e_c as one f32 fma chain over c = 0..d-1 starting from +0
  *   sigma = fp16(max_i |y_i| / 7), zc_i = clamp(rint(y_i * (1/sigma)), -7, 7) (all 0 if sigma == 0)
  * Dense values are copied into the cache layout; 2-bit values get the per-token quantizer over
- * 32-channel groups with the same numerics.
+ * 32-channel groups with the same numerics. Appends may be token-granular: every 32-token group
+ * that is whole once tokens [start, start + n_new) are in is encoded (its tokens before `start`
+ * are taken from the tails), and the tokens of an unfinished last group are copied exactly into
+ * ktail / vtail (rows t % 32). Appends to a stream must be sequential: the tails hold tokens
+ * [32 * floor(start / 32), start) from earlier calls.
  *   k        device keys, key_dtype, element (b, h, t, c) at k[b*ks[0] + h*ks[1] + t*ks[2] + c]
  *   k_strides element strides {batch, kv head, token}; channel stride is 1
  *   v        device values (value_dtype; f32 or bf16 also in 2-bit mode), or NULL to leave the
  *            value store untouched; v_strides as for keys (ignored when v is NULL)
- *   start, n_new  token range of every stream; both multiples of 32, start + n_new <= capacity
- * Errors: NULL, SHAPE, ALIGN (k, v and stride*element_size not multiples of 16 bytes, or
- * start/n_new not multiples of 32), CAPACITY, UNSUPPORTED, HIP. n_new == 0 is a no-op.
+ *   start, n_new  token range of every stream, start + n_new <= capacity
+ * Errors: NULL (also: a range that is not group-aligned without ktail, or without vtail when v is
+ * given), SHAPE, ALIGN (k, v and stride*element_size not multiples of 16 bytes), CAPACITY,
+ * UNSUPPORTED, HIP. n_new == 0 is a no-op.
  */
 headq_status headq_cache_append(const headq_config* cfg, const headq_cache* cache, const void* k,
                                 const int64_t k_strides[3], const void* v, const int64_t v_strides[3],
@@ -156,18 +165,20 @@ headq_status headq_cache_append(const headq_config* cfg, const headq_cache* cach
  * Computed in f32 with exact softmax over the n_ctx tokens, split over token ranges that are
  * merged by log-sum-exp.
  *   q           device [B][Hq][d] in query_dtype (contiguous)
- *   n_ctx       tokens attended: a positive multiple of 32, <= capacity
+ *   n_ctx       tokens attended, 1 <= n_ctx <= capacity; the n_ctx % 32 tokens past the last
+ *               whole group are read from ktail / vtail with exact keys and values (no side code)
  *   out         device [B][Hq][d] in out_dtype (HEADQ_F32 or HEADQ_BF16), contiguous
  *   corr_scale  multiplies the correction: 1 = HeadQ, 0 = base code only, -1 = wrong sign
  *   logits_dbg  device f32 [B][Hq][n_ctx] corrected logits in natural-log units, or NULL
- *   n_splits    token splits per (b, h); 0 = automatic, else 1..n_ctx/32 (at most 128 with
- *               dense bf16 or 2-bit values, the matrix-core path)
+ *   n_splits    token splits per (b, h); 0 = automatic, else 1..max(1, n_ctx/32) (at most 128
+ *               with dense bf16 or 2-bit values, the matrix-core path)
  *   ws, ws_bytes  device workspace. With ws == NULL the call only stores the bytes it needs in
  *               *ws_bytes and returns HEADQ_OK (nothing is launched). Otherwise *ws_bytes is
  *               the size of ws. The workspace must be zero-filled before its first use; every
  *               call leaves its leading counter region zero again, so one zeroed workspace
  *               serves any number of calls. Calls that share a workspace must not overlap.
- * Errors: NULL, SHAPE, ALIGN, CAPACITY, WORKSPACE, UNSUPPORTED, HIP.
+ * Errors: NULL (also: n_ctx % 32 != 0 without both tails), SHAPE, ALIGN, CAPACITY, WORKSPACE,
+ * UNSUPPORTED, HIP.
  */
 headq_status headq_decode_attn(const headq_config* cfg, const headq_cache* cache, const void* q,
                                int64_t n_ctx, void* out, int32_t out_dtype, float corr_scale, float* logits_dbg,
@@ -197,6 +208,12 @@ static inline size_t headq_vcode_bytes(const headq_config* c) {
 }
 static inline size_t headq_vmeta_bytes(const headq_config* c) {
   return (size_t)c->batch * c->n_kv_heads * c->capacity * (c->head_dim / 32) * 2 * 2;
+}
+static inline size_t headq_ktail_bytes(const headq_config* c) {
+  return (size_t)c->batch * c->n_kv_heads * 32 * c->head_dim * (c->key_dtype == HEADQ_F32 ? 4 : 2);
+}
+static inline size_t headq_vtail_bytes(const headq_config* c) {
+  return (size_t)c->batch * c->n_kv_heads * 32 * c->head_dim * (c->value_dtype == HEADQ_F32 ? 4 : 2);
 }
 
 #ifdef __cplusplus

@@ -46,7 +46,7 @@ class headq_cache(ctypes.Structure):
     _fields_ = [
         ("kcode", ctypes.c_void_p), ("kmeta", ctypes.c_void_p), ("scode", ctypes.c_void_p),
         ("ssc", ctypes.c_void_p), ("v", ctypes.c_void_p), ("vcode", ctypes.c_void_p),
-        ("vmeta", ctypes.c_void_p), ("U", ctypes.c_void_p),
+        ("vmeta", ctypes.c_void_p), ("U", ctypes.c_void_p), ("ktail", ctypes.c_void_p), ("vtail", ctypes.c_void_p),
     ]
 
 
@@ -142,7 +142,8 @@ def _strides3(t):
 
 
 def headq_cache_append(cfg: Config, cache: headq_cache, k, v=None, start: int = 0, stream=None):
-    """Quantize and store k (and v) [B][Hkv][n_new][d] (torch device tensors) at token `start`."""
+    """Append k (and v) [B][Hkv][n_new][d] (torch device tensors) at token `start`: whole groups
+    are encoded, the tokens of an unfinished last group go to the dense tails."""
     c = cfg.c()
     ks = _strides3(k)
     vs = _strides3(v) if v is not None else None
@@ -191,6 +192,10 @@ class DeviceCache:
         else:
             self.vcode = torch.zeros((B, H, cap // GROUP, d * 8), dtype=u8, device=device)
             self.vmeta = torch.zeros((B, H, cap // GROUP, 2, d // GROUP, GROUP), dtype=i16, device=device)
+        kdt = torch.float32 if cfg.key_dtype == HEADQ_F32 else torch.bfloat16
+        vdt = torch.float32 if cfg.value_dtype == HEADQ_F32 else torch.bfloat16
+        self.ktail = torch.zeros((B, H, GROUP, d), dtype=kdt, device=device)
+        self.vtail = torch.zeros((B, H, GROUP, d), dtype=vdt, device=device)
         self.U = None
 
     def set_basis(self, U):
@@ -199,7 +204,7 @@ class DeviceCache:
 
     def c(self) -> headq_cache:
         return headq_cache(_ptr(self.kcode), _ptr(self.kmeta), _ptr(self.scode), _ptr(self.ssc), _ptr(self.v),
-                           _ptr(self.vcode), _ptr(self.vmeta), _ptr(self.U))
+                           _ptr(self.vcode), _ptr(self.vmeta), _ptr(self.U), _ptr(self.ktail), _ptr(self.vtail))
 
     def append(self, k, v=None, start: int = 0, stream=None):
         headq_cache_append(self.cfg, self.c(), k, v, start, stream)
@@ -218,4 +223,5 @@ class DeviceCache:
 
     def nbytes(self) -> int:
         return sum(t.numel() * t.element_size() for t in (self.kcode, self.kmeta, self.scode, self.ssc, self.v,
-                                                           self.vcode, self.vmeta) if t is not None)
+                                                           self.vcode, self.vmeta, self.ktail, self.vtail)
+                   if t is not None)

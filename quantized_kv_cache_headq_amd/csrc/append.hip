@@ -59,56 +59,94 @@ __device__ __forceinline__ uint32_t base_code(float k, float z, float inv) {
   return (uint32_t)c;
 }
 
-// The workgroup's two groups: row = 32 * gl + t. Group gl is group 2 * blockIdx.x + gl of the
-// appended range, clamped to the last one (a duplicate whose stores are masked) when the range
-// holds an odd number of groups. (Plain scalars with selects: a small array indexed by a lane
-// value would live in scratch memory.)
+// The workgroup's two groups: row = 32 * gl + t. The appended range [start, end) touches groups
+// floor(start/32) .. ceil(end/32)-1; group gl of this workgroup is touched group 2*blockIdx.x + gl,
+// clamped to the last one (a duplicate whose stores are masked) when the count is odd. A group is
+// encoded only if it is whole once the range is in (32 * (g + 1) <= end); the rows of a group
+// before `start` come from the dense tail, rows at or past `end` do not exist yet. (Plain scalars
+// with selects: a small array indexed by a lane value would live in scratch memory.)
 struct Tile {
   int64_t bh;
-  int64_t g0, g1;  // range groups of rows 0..31 and 32..63
-  bool v1;         // the second group is real
-  __device__ int64_t g_rel(int gl) const { return gl ? g1 : g0; }
-  __device__ bool valid(int gl) const { return gl ? v1 : true; }
+  int64_t g0, g1;  // cache groups of rows 0..31 and 32..63
+  bool w0, w1;     // the group is whole and real: it is encoded and stored
+  __device__ int64_t group(int gl) const { return gl ? g1 : g0; }
+  __device__ bool whole(int gl) const { return gl ? w1 : w0; }
 };
 
 __device__ __forceinline__ Tile tile_of(const AppendArgs& a) {
   Tile tl;
   tl.bh = (int64_t)blockIdx.z * a.hkv + blockIdx.y;
-  const int64_t n_groups = a.n_new / kGroup;
-  tl.g0 = (int64_t)blockIdx.x * kGpw;
-  tl.v1 = tl.g0 + 1 < n_groups;
-  tl.g1 = tl.v1 ? tl.g0 + 1 : tl.g0;
+  const int64_t end = a.start + a.n_new;
+  const int64_t g_first = a.start / kGroup, n_touch = (end + kGroup - 1) / kGroup - g_first;
+  tl.g0 = g_first + (int64_t)blockIdx.x * kGpw;
+  const bool real1 = (int64_t)blockIdx.x * kGpw + 1 < n_touch;
+  tl.g1 = real1 ? tl.g0 + 1 : tl.g0;
+  tl.w0 = (tl.g0 + 1) * kGroup <= end;
+  tl.w1 = real1 && (tl.g1 + 1) * kGroup <= end;
   return tl;
 }
 
-// Token (within the appended range) of LDS row `row`.
+// Cache token of LDS row `row`.
 __device__ __forceinline__ int64_t row_token(const Tile& tl, int row) {
-  return tl.g_rel(row / kGroup) * kGroup + row % kGroup;
+  return tl.group(row / kGroup) * kGroup + row % kGroup;
+}
+
+// Address of 16 bytes at element `c` of cache token `tok`'s row for a given input: the dense
+// tail (tokens before `start`), the caller's rows (tokens in [start, end)), or nullptr (tokens
+// past `end`, which do not exist yet). `es` is the element size, `base` the caller's (b, h) row 0.
+__device__ __forceinline__ const void* row_src(const AppendArgs& a, const void* base, int64_t ts, const void* tail,
+                                               int64_t bh, int D, int es, int64_t tok, int c) {
+  if (tok < a.start) return (const char*)tail + ((bh * kGroup + tok % kGroup) * D + c) * es;
+  if (tok < a.start + a.n_new) return (const char*)base + ((tok - a.start) * ts + c) * es;
+  return nullptr;
 }
 
 // Load the 64 rows of f32/bf16 input (element stride 1 along channels, token stride ts) into an
-// f32 LDS tile with row pitch P, with 128-bit loads.
+// f32 LDS tile with row pitch P, with 128-bit loads; rows that do not exist yet read as zero.
 template <int D, int P, bool BF16>
-__device__ __forceinline__ void load_rows(float (*dst)[P], const void* base, int64_t ts, const Tile& tl) {
+__device__ __forceinline__ void load_rows(float (*dst)[P], const AppendArgs& a, const void* base, int64_t ts,
+                                          const void* tail, const Tile& tl) {
   constexpr int kElem = BF16 ? 8 : 4;  // elements per 16-byte load
   constexpr int kChunks = D / kElem;   // 16-byte chunks per row
   for (int i = threadIdx.x; i < kRows * kChunks; i += kThreads) {
     const int row = i / kChunks, ch = i % kChunks;
-    const int64_t tok = row_token(tl, row);
+    const void* src = row_src(a, base, ts, tail, tl.bh, D, BF16 ? 2 : 4, row_token(tl, row), ch * kElem);
+    const uint4 w = src ? *reinterpret_cast<const uint4*>(src) : make_uint4(0u, 0u, 0u, 0u);
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
     if constexpr (BF16) {
-      const uint4 w = *reinterpret_cast<const uint4*>((const uint16_t*)base + tok * ts + ch * kElem);
-      const uint32_t u[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         dst[row][ch * 8 + 2 * j] = __uint_as_float(u[j] << 16);
         dst[row][ch * 8 + 2 * j + 1] = __uint_as_float(u[j] & 0xffff0000u);
       }
     } else {
-      const float4 w = *reinterpret_cast<const float4*>((const float*)base + tok * ts + ch * kElem);
-      dst[row][ch * 4 + 0] = w.x;
-      dst[row][ch * 4 + 1] = w.y;
-      dst[row][ch * 4 + 2] = w.z;
-      dst[row][ch * 4 + 3] = w.w;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dst[row][ch * 4 + j] = __uint_as_float(u[j]);
+    }
+  }
+}
+
+// Copy the caller's rows of the unfinished last group into the dense tails (rows t % 32).
+// Done by workgroup 0 only, after every read of the tails in this launch: the only group that
+// reads tail rows is the first touched one, which workgroup 0 owns.
+__device__ __forceinline__ void write_tails(const AppendArgs& a, int64_t bh, int D, const void* kbase, int kes,
+                                            const void* vbase, int ves) {
+  const int64_t end = a.start + a.n_new;
+  if (end % kGroup == 0) return;
+  const int64_t t_lo = a.start > end / kGroup * kGroup ? a.start : end / kGroup * kGroup;
+  const int n_rows = (int)(end - t_lo);
+  for (int pass = 0; pass < 2; ++pass) {
+    const int es = pass ? ves : kes;
+    const char* src = (const char*)(pass ? vbase : kbase);
+    char* tail = (char*)(pass ? a.vtail : a.ktail);
+    const int64_t ts = pass ? a.vs_t : a.ks_t;
+    if (!src) continue;
+    const int chunks = D * es / 16;
+    for (int i = threadIdx.x; i < n_rows * chunks; i += kThreads) {
+      const int64_t tok = t_lo + i / chunks;
+      const int ch = i % chunks;
+      *reinterpret_cast<uint4*>(tail + (bh * kGroup + tok % kGroup) * D * es + ch * 16) =
+          *reinterpret_cast<const uint4*>(src + (tok - a.start) * ts * es + ch * 16);
     }
   }
 }
@@ -133,7 +171,14 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
   const int h = blockIdx.y, b = blockIdx.z;
   const int64_t groups_cap = a.cap / kGroup;
-  const int64_t g_abs0 = tl.bh * groups_cap + a.start / kGroup;  // cache group of range group 0
+  const int64_t gs0 = tl.bh * groups_cap;  // cache group 0 of this stream
+  const char* kin = (const char*)a.k + ((int64_t)b * a.ks_b + (int64_t)h * a.ks_h) * (KBF16 ? 2 : 4);
+  const int ves = a.value_bf16 ? 2 : 4;
+  const char* vin = a.v ? (const char*)a.v + ((int64_t)b * a.vs_b + (int64_t)h * a.vs_h) * ves : nullptr;
+  if (!tl.w0) {  // no whole group here (the second one cannot be whole either): tail rows only
+    if (blockIdx.x == 0) write_tails(a, tl.bh, D, kin, KBF16 ? 2 : 4, vin, ves);
+    return;
+  }
 
   // value rows requested first, into registers: their latency overlaps the whole key pipeline
   constexpr int VMAX = D / 16;                  // 16-byte chunks per thread for f32 values
@@ -141,21 +186,19 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
   const int vper = vbf ? 8 : 4;                 // elements per chunk
   const int vchunks = D / vper;                 // chunks per row
   const int vpt = kRows * vchunks / kThreads;   // chunks per thread
-  const int64_t vbase = (int64_t)b * a.vs_b + (int64_t)h * a.vs_h;
   uint4 vr[VMAX];
   if (a.v) {
 #pragma unroll
     for (int k = 0; k < VMAX; ++k) {
       if (k < vpt) {
         const int i = tid + k * kThreads, row = i / vchunks, c0 = (i % vchunks) * vper;
-        const char* src = (const char*)a.v + (vbase + row_token(tl, row) * a.vs_t + c0) * (vbf ? 2 : 4);
-        vr[k] = *reinterpret_cast<const uint4*>(src);
+        const void* src = row_src(a, vin, a.vs_t, a.vtail, tl.bh, D, ves, row_token(tl, row), c0);
+        vr[k] = src ? *reinterpret_cast<const uint4*>(src) : make_uint4(0u, 0u, 0u, 0u);
       }
     }
   }
 
-  const char* kin = (const char*)a.k + ((int64_t)b * a.ks_b + (int64_t)h * a.ks_h) * (KBF16 ? 2 : 4);
-  load_rows<D, P, KBF16>(ke, kin, a.ks_t, tl);
+  load_rows<D, P, KBF16>(ke, a, kin, a.ks_t, a.ktail, tl);
   if constexpr (UL && R > 0) {
     const float4* Ug = reinterpret_cast<const float4*>(a.U + (int64_t)h * D * R);
     for (int i = tid; i < D * R / 4; i += kThreads) reinterpret_cast<float4*>(U_s)[i] = Ug[i];
@@ -174,8 +217,8 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
     float s, z, inv;
     uint16_t sb, zb;
     minmax_step_zero(lo, hi, 3.0f, s, z, inv, sb, zb);
-    if (tl.valid(gl)) {
-      uint16_t* meta = a.kmeta + (g_abs0 + tl.g_rel(gl)) * 2 * D;
+    if (tl.whole(gl)) {
+      uint16_t* meta = a.kmeta + (gs0 + tl.group(gl)) * 2 * D;
       meta[c] = sb;
       meta[D + c] = zb;
     }
@@ -197,8 +240,8 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
       word |= code << kcode_bit(j);
       ke[row][c] = k - __builtin_fmaf((float)code, s_s[m], z_s[m]);
     }
-    if (tl.valid(gl)) {
-      const int64_t tok = a.start + row_token(tl, row);
+    if (tl.whole(gl)) {
+      const int64_t tok = row_token(tl, row);
       *reinterpret_cast<uint32_t*>(a.kcode + (tl.bh * a.cap + tok) * (D / 4) + c0 / 4) = word;
     }
   }
@@ -254,8 +297,8 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
         zc = zc > 7.0f ? 7.0f : zc;
         packed |= (uint32_t)((int)zc + 8) << (4 * j);
       }
-      if (tl.valid(gl)) {
-        const int64_t tok = a.start + row_token(tl, row);
+      if (tl.whole(gl)) {
+        const int64_t tok = row_token(tl, row);
         uint8_t* dst = a.scode + (tl.bh * a.cap + tok) * (R / 2) + wave * (CW / 2);
         if constexpr (CW == 8)
           *reinterpret_cast<uint32_t*>(dst) = packed;
@@ -267,8 +310,7 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
       }
     }
   }
-  if (!a.v) return;
-
+  if (a.v) {
   // 5. values of the same rows (LDS reused once every wave is done with the residuals)
   __syncthreads();
   if (a.value_mode == HEADQ_V_DENSE) {
@@ -294,8 +336,8 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
     __syncthreads();
     for (int i = tid; i < kRows * D; i += kThreads) {
       const int gl = i / (D * kGroup), c = (i / kGroup) % D, t = i % kGroup;
-      if (!tl.valid(gl)) continue;
-      const int64_t idx = ((g_abs0 + tl.g_rel(gl)) * D + c) * kGroup + t;
+      if (!tl.whole(gl)) continue;
+      const int64_t idx = ((gs0 + tl.group(gl)) * D + c) * kGroup + t;
       const uint32_t x = raw[gl * kGroup + t][c];
       if (vbf)
         ((uint16_t*)a.vdense)[idx] = (uint16_t)x;
@@ -334,8 +376,8 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
       float s, z, inv;
       uint16_t sb, zb;
       minmax_step_zero(lo, hi, 3.0f, s, z, inv, sb, zb);
-      if (tl.valid(gl)) {
-        const int64_t gabs = g_abs0 + tl.g_rel(gl);
+      if (tl.whole(gl)) {
+        const int64_t gabs = gs0 + tl.group(gl);
         a.vmeta[(gabs * 2 + 0) * NG * kGroup + gc * kGroup + t] = sb;
         a.vmeta[(gabs * 2 + 1) * NG * kGroup + gc * kGroup + t] = zb;
       }
@@ -360,15 +402,22 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
           const int row = gl * kGroup + t0 + 4 * q + e;
           v |= base_code(ke[row][c], z_s[row * NG + gc], inv_s[row * NG + gc]) << (4 * e + 2 * q);
         }
-      if (tl.valid(gl)) a.vcode[(g_abs0 + tl.g_rel(gl)) * D * 8 + byte] = (uint8_t)v;
+      if (tl.whole(gl)) a.vcode[(gs0 + tl.group(gl)) * D * 8 + byte] = (uint8_t)v;
     }
+  }
+  }  // values
+
+  if (blockIdx.x == 0 && (a.start + a.n_new) % kGroup) {
+    __syncthreads();  // every tail row this workgroup read has been consumed
+    write_tails(a, tl.bh, D, kin, KBF16 ? 2 : 4, vin, ves);
   }
 }
 
 template <int D, int R>
 hipError_t launch_dr(const AppendArgs& a, hipStream_t s) {
-  const int64_t n_groups = a.n_new / kGroup;
-  dim3 grid((unsigned)((n_groups + kGpw - 1) / kGpw), (unsigned)a.hkv, (unsigned)a.batch);
+  const int64_t end = a.start + a.n_new;
+  const int64_t n_touch = (end + kGroup - 1) / kGroup - a.start / kGroup;  // groups the range touches
+  dim3 grid((unsigned)((n_touch + kGpw - 1) / kGpw), (unsigned)a.hkv, (unsigned)a.batch);
   const bool small = (int64_t)grid.x * grid.y * grid.z <= 1024;  // at most ~4 workgroups per CU
   if (a.key_bf16) {
     if (small)

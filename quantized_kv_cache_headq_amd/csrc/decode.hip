@@ -82,14 +82,34 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
   for (int j = 0; j < HPT; ++j) o[j] = 0.0f;
 
+  // whole groups, then (index n_groups) the unfinished group held exactly in the tails
   const int64_t n_groups = a.n_ctx / kGroup;
+  const int tail_len = (int)(a.n_ctx % kGroup);
+  const int64_t n_units = n_groups + (tail_len ? 1 : 0);
   const int64_t g_begin = (int64_t)split * a.groups_per_split;
   int64_t g_end = g_begin + a.groups_per_split;
-  if (g_end > n_groups) g_end = n_groups;
+  if (g_end > n_units) g_end = n_units;
 
   for (int64_t gi = g_begin; gi < g_end; ++gi) {
+    const bool is_tail = gi == n_groups;
     __syncthreads();  // previous group fully consumed
-    if (tid < D) {
+    if (is_tail) {
+      // A (tail): exact logits q.k over the tail rows; rows past n_ctx get -inf
+      const int t = tid / 8, sub = tid % 8;
+      for (int hh = sub; hh < g; hh += 8) {
+        float acc = -INFINITY;
+        if (t < tail_len) {
+          acc = 0.0f;
+          const int64_t row = (bh * kGroup + t) * D;
+          for (int c = 0; c < D; ++c) {
+            const float k = a.key_bf16 ? bf16_to_f32(((const uint16_t*)a.ktail)[row + c]) : ((const float*)a.ktail)[row + c];
+            acc = fmaf(qbar[hh][c], k, acc);
+          }
+          if (a.logits_dbg) a.logits_dbg[((int64_t)b * a.hq + hq0 + hh) * a.n_ctx + gi * kGroup + t] = acc * kLn2;
+        }
+        sc[hh][t] = acc;
+      }
+    } else if (tid < D) {
       const uint16_t* meta = a.kmeta + (bh * (a.cap / kGroup) + gi) * 2 * D;
       sz[0][tid] = f16_bits_to_f32(meta[tid]);
       sz[1][tid] = f16_bits_to_f32(meta[D + tid]);
@@ -97,7 +117,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
     __syncthreads();
 
     // A: logits. thread (token t, heads sub, sub + 8)
-    {
+    if (!is_tail) {
       const int t = tid / 8, sub = tid % 8;
       const int64_t tok = gi * kGroup + t;
       const uint32_t* kc = (const uint32_t*)(a.kcode + (bh * a.cap + tok) * (D / 4));
@@ -165,7 +185,15 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
     {
       float v[kGroup];
       const int64_t gabs = bh * (a.cap / kGroup) + gi;
-      if constexpr (VMODE == HEADQ_V_DENSE) {
+      if (is_tail) {
+        // exact tail values, zero past n_ctx (their probabilities are 0)
+#pragma unroll
+        for (int t = 0; t < kGroup; ++t) {
+          const int64_t idx = (bh * kGroup + t) * D + c_own;
+          v[t] = t >= tail_len ? 0.0f
+                 : a.value_bf16 ? bf16_to_f32(((const uint16_t*)a.vtail)[idx]) : ((const float*)a.vtail)[idx];
+        }
+      } else if constexpr (VMODE == HEADQ_V_DENSE) {
         if constexpr (VBF16) {
           const uint4* src = (const uint4*)((const uint16_t*)a.vdense + (gabs * D + c_own) * kGroup);
 #pragma unroll

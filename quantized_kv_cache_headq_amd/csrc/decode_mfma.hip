@@ -430,6 +430,109 @@ __device__ __forceinline__ void process_group(const GroupRaw<D, R, VQ2>& cur, co
   }
 }
 
+// The unfinished last group: n_ctx % 32 tokens whose keys and values are held exactly in the
+// tails (no base or side code). On the vector units, once per stream: lane (n, quad) scores tokens
+// 8*quad .. +7 for head n with the scaled query, takes the same online-softmax step as a group, and
+// adds p . v to its own output channels 16*ct + 4*quad + j, fetching the other quads'
+// probabilities by lane shuffles.
+template <int D>
+__device__ __forceinline__ void process_tail(const DecodeArgs& a, int64_t bh, int b, int hq0, int g, int n,
+                                             int quad, const float (*qs)[D], float inv_scale, floatx4* o_acc,
+                                             float* z_acc, int n_z, float& m_run, float& l_run) {
+  constexpr int NCT = D / 16;
+  const int64_t n_full = a.n_ctx / kGroup * kGroup;
+  const int tail_len = (int)(a.n_ctx - n_full);
+  // scores of rows 8*quad + j: channels in steps of 8 (one 16-byte or two 16-byte loads per row)
+  float acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+#pragma unroll 1
+  for (int c = 0; c < D; c += 8) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int t = 8 * quad + j;
+      if (t >= tail_len) continue;
+      const int64_t row = (bh * kGroup + t) * D + c;
+      float k[8];
+      if (a.key_bf16) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>((const uint16_t*)a.ktail + row);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          k[2 * i] = __uint_as_float(w[i] << 16);
+          k[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+      } else {
+        const floatx4 w0 = *reinterpret_cast<const floatx4*>((const float*)a.ktail + row);
+        const floatx4 w1 = *reinterpret_cast<const floatx4*>((const float*)a.ktail + row + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          k[i] = w0[i];
+          k[4 + i] = w1[i];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[j] = fmaf(qs[n][c + i], k[i], acc[j]);
+    }
+  }
+  float sv[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int t = 8 * quad + j;
+    sv[j] = t < tail_len ? inv_scale * acc[j] : -INFINITY;
+    if (t < tail_len && a.logits_dbg && n < g)
+      a.logits_dbg[((int64_t)b * a.hq + hq0 + n) * a.n_ctx + n_full + t] = sv[j] * kLn2;
+  }
+  // online softmax step (as for a group)
+  float mx = sv[0];
+#pragma unroll
+  for (int j = 1; j < 8; ++j) mx = fmaxf(mx, sv[j]);
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const bool grow = mx > m_run + kLazyMax;
+  if (__any(grow)) {
+    const float m_new = grow ? mx : m_run;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) o_acc[ct] *= alpha;
+    for (int cg = 0; cg < n_z; ++cg) z_acc[cg] *= alpha;
+  }
+  float p[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    p[j] = __builtin_amdgcn_exp2f(sv[j] - m_run);  // 0 for the rows past n_ctx
+    l_run += p[j];
+  }
+#pragma unroll 1
+  for (int t = 0; t < tail_len; ++t) {
+    // row t's probability for head n lives in lane n + 16 * (t / 8), slot t % 8
+    const int js = t % 8;
+    float pj = p[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) pj = js == j ? p[j] : pj;
+    const float pt = __shfl(pj, n + 16 * (t / 8));
+    const int64_t row = (bh * kGroup + t) * D + 4 * quad;
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      float v[4];
+      if (a.value_bf16) {
+        const u32x2 w = *reinterpret_cast<const u32x2*>((const uint16_t*)a.vtail + row + 16 * ct);
+        v[0] = __uint_as_float(w[0] << 16);
+        v[1] = __uint_as_float(w[0] & 0xffff0000u);
+        v[2] = __uint_as_float(w[1] << 16);
+        v[3] = __uint_as_float(w[1] & 0xffff0000u);
+      } else {
+        const floatx4 w = *reinterpret_cast<const floatx4*>((const float*)a.vtail + row + 16 * ct);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = w[i];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o_acc[ct][i] = fmaf(pt, v[i], o_acc[ct][i]);
+    }
+  }
+}
+
 template <int D, int R, bool VQ2>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int NKT = D / 32, NCT = D / 16, NG = D / 32;
@@ -489,12 +592,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // group indices are 32-bit and wave-uniform, so every offset below stays in scalar registers
   const int n_groups = (int)(a.n_ctx / kGroup);
   const int W = a.n_splits * kWaves;
-  const int rot = (int)((bh * 40503) % n_groups);
+  const int rot = n_groups > 0 ? (int)((bh * 40503) % n_groups) : 0;
   auto group_at = [&](int j) { const int x = j + rot; return x >= n_groups ? x - n_groups : x; };
   const int j_begin = split * kWaves + wave;
   GroupRaw<D, R, VQ2> ga, gb;  // ping-pong register sets: one group computed while the next loads
-  if (j_begin < n_groups) load_group<D, R, VQ2>(ga, s, lane, n, quad, group_at(j_begin));
-  if (j_begin + W < n_groups) load_group<D, R, VQ2>(gb, s, lane, n, quad, group_at(j_begin + W));
+  // the wave that takes the unfinished group requests its first groups after it (fewer live registers)
+  const bool tail_wave = a.n_ctx % kGroup && split == 0 && wave == 0;
+  if (!tail_wave) {
+    if (j_begin < n_groups) load_group<D, R, VQ2>(ga, s, lane, n, quad, group_at(j_begin));
+    if (j_begin + W < n_groups) load_group<D, R, VQ2>(gb, s, lane, n, quad, group_at(j_begin + W));
+  }
   __syncthreads();
 
   // ---- prologue (whole workgroup): per-head power-of-two query scale, U^T q
@@ -557,6 +664,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
   for (int cg = 0; cg < NG; ++cg) z_acc[cg] = 0.0f;
   float m_run = -INFINITY, l_run = 0.0f;
+
+  // ---- the unfinished last group (exact, from the tails), by one wave per stream
+  if (tail_wave) {
+    process_tail<D>(a, bh, b, hq0, g, n, quad, qs, f.inv_scale, o_acc, z_acc, VQ2 ? NG : 0, m_run, l_run);
+    if (j_begin < n_groups) load_group<D, R, VQ2>(ga, s, lane, n, quad, group_at(j_begin));
+    if (j_begin + W < n_groups) load_group<D, R, VQ2>(gb, s, lane, n, quad, group_at(j_begin + W));
+  }
 
   // ---- this wave's groups
   uint8_t* slot = reinterpret_cast<uint8_t*>(kslot[wave]);

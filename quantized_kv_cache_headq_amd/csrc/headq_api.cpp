@@ -53,7 +53,7 @@ headq_status check_cache(const headq_config* c, const headq_cache* k) {
   if (c->rank > 0 && (!k->scode || !k->ssc || !k->U)) return HEADQ_ERR_NULL;
   if (c->value_mode == HEADQ_V_DENSE && !k->v) return HEADQ_ERR_NULL;
   if (c->value_mode == HEADQ_V_Q2 && (!k->vcode || !k->vmeta)) return HEADQ_ERR_NULL;
-  const void* ptrs[] = {k->kcode, k->kmeta, k->scode, k->ssc, k->v, k->vcode, k->vmeta, k->U};
+  const void* ptrs[] = {k->kcode, k->kmeta, k->scode, k->ssc, k->v, k->vcode, k->vmeta, k->U, k->ktail, k->vtail};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return HEADQ_ERR_ALIGN;
   return HEADQ_OK;
@@ -66,7 +66,7 @@ extern "C" const char* headq_status_string(headq_status s) {
     case HEADQ_OK: return "ok";
     case HEADQ_ERR_NULL: return "required pointer is NULL";
     case HEADQ_ERR_SHAPE: return "inconsistent or out-of-range dimensions";
-    case HEADQ_ERR_ALIGN: return "token count/offset not a multiple of 32 or buffer not 16-byte aligned";
+    case HEADQ_ERR_ALIGN: return "buffer, stride or capacity not aligned (16 bytes; capacity a multiple of 32)";
     case HEADQ_ERR_CAPACITY: return "token range exceeds the cache capacity";
     case HEADQ_ERR_WORKSPACE: return "workspace too small";
     case HEADQ_ERR_NUMERIC: return "non-finite input";
@@ -86,8 +86,10 @@ extern "C" headq_status headq_cache_append(const headq_config* cfg, const headq_
   st = check_cache(cfg, cache);
   if (st != HEADQ_OK) return st;
   if (start < 0 || n_new < 0) return HEADQ_ERR_SHAPE;
-  if (start % headq::kGroup || n_new % headq::kGroup) return HEADQ_ERR_ALIGN;
   if (start + n_new > cfg->capacity) return HEADQ_ERR_CAPACITY;
+  // a range that starts or ends inside a group goes through the dense tails
+  const bool group_aligned = start % headq::kGroup == 0 && (start + n_new) % headq::kGroup == 0;
+  if (!group_aligned && (!cache->ktail || (v && !cache->vtail))) return HEADQ_ERR_NULL;
   const int kes = cfg->key_dtype == HEADQ_F32 ? 4 : 2;
   const int ves = cfg->value_dtype == HEADQ_F32 ? 4 : 2;
   if (!aligned16(k)) return HEADQ_ERR_ALIGN;
@@ -135,6 +137,8 @@ extern "C" headq_status headq_cache_append(const headq_config* cfg, const headq_
   a.vcode = cache->vcode;
   a.vmeta = cache->vmeta;
   a.U = cache->U;
+  a.ktail = cache->ktail;
+  a.vtail = cache->vtail;
   hipStream_t s = (hipStream_t)stream;
   return finish(headq::launch_append(a, s), s);
 }
@@ -176,14 +180,16 @@ extern "C" headq_status headq_decode_attn(const headq_config* cfg, const headq_c
   if (st != HEADQ_OK) return st;
   if (!ws_bytes) return HEADQ_ERR_NULL;
   if (n_ctx < 1) return HEADQ_ERR_SHAPE;
-  if (n_ctx % headq::kGroup) return HEADQ_ERR_ALIGN;
+
   if (n_ctx > cfg->capacity) return HEADQ_ERR_CAPACITY;
   if (out_dtype != HEADQ_F32 && out_dtype != HEADQ_BF16) return HEADQ_ERR_UNSUPPORTED;
-  const int64_t n_groups = n_ctx / headq::kGroup;
-  if (n_splits < 0 || n_splits > n_groups) return HEADQ_ERR_SHAPE;
+  const int64_t n_groups = n_ctx / headq::kGroup;  // whole groups; the rest is in the tails
+  // work units for the split: the whole groups plus the unfinished one held in the tails
+  const int64_t n_units = n_groups + (n_ctx % headq::kGroup ? 1 : 0);
+  if (n_splits < 0 || n_splits > n_units) return HEADQ_ERR_SHAPE;
   const bool mfma = decode_uses_mfma(cfg);
   const int chunks = mfma ? 4 : 1;
-  const int S = n_splits ? n_splits : auto_splits(cfg, n_groups, chunks, mfma);
+  const int S = n_splits ? n_splits : auto_splits(cfg, n_units, chunks, mfma);
   if (mfma && S > headq::kMaxSplitsMfma) return HEADQ_ERR_UNSUPPORTED;
   const size_t need = headq::decode_ws_bytes(cfg->batch, cfg->n_q_heads, cfg->n_kv_heads, cfg->head_dim, S);
   if (!ws) {
@@ -193,6 +199,7 @@ extern "C" headq_status headq_decode_attn(const headq_config* cfg, const headq_c
   if (!cache || !q || !out) return HEADQ_ERR_NULL;
   st = check_cache(cfg, cache);
   if (st != HEADQ_OK) return st;
+  if (n_ctx % headq::kGroup && (!cache->ktail || !cache->vtail)) return HEADQ_ERR_NULL;
   if (*ws_bytes < need) return HEADQ_ERR_WORKSPACE;
   if (!aligned16(q) || !aligned16(out) || !aligned16(ws) || (logits_dbg && !aligned16(logits_dbg)))
     return HEADQ_ERR_ALIGN;
@@ -209,7 +216,7 @@ extern "C" headq_status headq_decode_attn(const headq_config* cfg, const headq_c
   a.n_splits = S;
   a.chunks_per_split = chunks;
   a.use_mfma = mfma;
-  a.groups_per_split = (int)((n_groups + (int64_t)S * chunks - 1) / ((int64_t)S * chunks));
+  a.groups_per_split = (int)((n_units + (int64_t)S * chunks - 1) / ((int64_t)S * chunks));
   a.query_bf16 = cfg->query_dtype == HEADQ_BF16;
   a.value_bf16 = cfg->value_dtype == HEADQ_BF16;
   a.value_mode = cfg->value_mode;
@@ -224,6 +231,9 @@ extern "C" headq_status headq_decode_attn(const headq_config* cfg, const headq_c
   a.vcode = cache->vcode;
   a.vmeta = cache->vmeta;
   a.U = cache->U;
+  a.ktail = cache->ktail;
+  a.vtail = cache->vtail;
+  a.key_bf16 = cfg->key_dtype == HEADQ_BF16;
   a.logits_dbg = logits_dbg;
   a.ws_count = (uint32_t*)ws;
   a.ws_o = (float*)((char*)ws + headq::decode_ws_counter_bytes(cfg->batch, cfg->n_kv_heads));

@@ -45,6 +45,8 @@ struct AppendArgs {
   uint8_t* vcode;
   uint16_t* vmeta;
   const float* U;
+  void* ktail;                 // [B][Hkv][32][d] key_dtype: tokens of the unfinished last group
+  void* vtail;                 // [B][Hkv][32][d] value_dtype
 };
 
 struct DecodeArgs {
@@ -65,6 +67,9 @@ struct DecodeArgs {
   const uint8_t* vcode;
   const uint16_t* vmeta;
   const float* U;
+  const void* ktail;           // tail of the unfinished group (n_ctx % 32 tokens), exact
+  const void* vtail;
+  int key_bf16;                // dtype of ktail
   float* logits_dbg;           // may be null
   uint32_t* ws_count;          // [B][Hkv] arrival counters (zero between calls)
   float* ws_o;                 // [B][Hq][S][d]

@@ -72,7 +72,7 @@ def host(t, view_u16=False):
 def compare_cache(dc, oc, streams=None):
     """Bit-exact comparison of every cache buffer (optionally only some (b, h) streams)."""
     pairs = [("kcode", dc.kcode), ("kmeta", dc.kmeta), ("scode", dc.scode), ("ssc", dc.ssc), ("v", dc.v),
-             ("vcode", dc.vcode), ("vmeta", dc.vmeta)]
+             ("vcode", dc.vcode), ("vmeta", dc.vmeta), ("ktail", dc.ktail), ("vtail", dc.vtail)]
     for name, t in pairs:
         if t is None or name not in oc or oc[name].size == 0:
             continue
@@ -81,7 +81,7 @@ def compare_cache(dc, oc, streams=None):
         if streams is not None:
             g = np.stack([g[b, h] for b, h in streams])
             o = np.stack([o[b, h] for b, h in streams])
-        if name == "v" and g.dtype == np.float32:
+        if g.dtype == np.float32:
             g, o = g.view(np.uint32), o.view(np.uint32)
         assert g.shape == o.shape, (name, g.shape, o.shape)
         bad = np.argwhere(g != o)

@@ -139,8 +139,8 @@ def test_append_validation_statuses():
     assert _append_status(_cfg(n_q_heads=6, n_kv_heads=4), cache, k) == 2     # Hq % Hkv
     assert _append_status(_cfg(n_q_heads=34, n_kv_heads=2), cache, k) == 7    # g > 16
     assert _append_status(_cfg(capacity=100), cache, k) == 3                  # capacity % 32
-    assert _append_status(cfg, cache, k, start=16) == 3                       # start % 32
-    assert _append_status(cfg, cache, k, n_new=48) == 3                       # n_new % 32
+    assert _append_status(cfg, cache, k, start=16) == 1                       # inside a group, no tails
+    assert _append_status(cfg, cache, k, n_new=48) == 1                       # ends inside a group, no tails
     assert _append_status(cfg, cache, k, start=96) == 4                       # start + n > cap
     assert _append_status(cfg, cache, _fake_keys(cfg, align=4)) == 3          # misaligned keys
     bad = bd.headq_cache(0x10000004, 0x10001000, 0x10002000, 0x10003000, 0x10004000, 0, 0, 0x10007000)
@@ -171,10 +171,11 @@ def test_decode_workspace_query_and_validation():
     st1, nb1 = _decode_status(cfg, ws=None, nbytes=0, n_splits=1)
     assert st1 == 0 and nb1 == 256 + 2 * 4 * 1 * (64 + 2) * 4  # counters (padded), then partials
     assert _decode_status(cfg, nbytes=nb1 - 4, n_splits=1)[0] == 5           # workspace too small
-    assert _decode_status(cfg, n_ctx=48)[0] == 3                              # n_ctx % 32
+    assert _decode_status(cfg, n_ctx=48)[0] == 1                              # n_ctx % 32 without tails
     assert _decode_status(cfg, n_ctx=160)[0] == 4                             # n_ctx > capacity
     assert _decode_status(cfg, n_ctx=0)[0] == 2
     assert _decode_status(cfg, n_splits=3)[0] == 2                            # more splits than groups
+    assert _decode_status(cfg, n_ctx=48, n_splits=3)[0] == 2                  # 1 whole group + the tail
     assert _decode_status(cfg, q=0x30000002)[0] == 3                          # misaligned query
     assert _decode_status(cfg, out_dtype=5)[0] == 7
     assert _decode_status(cfg, q=None)[0] == 1
