@@ -149,13 +149,17 @@ headq_status headq_calibrate(const headq_config* cfg, const float* q_cal, int64_
  *   v        device values (value_dtype; f32 or bf16 also in 2-bit mode), or NULL to leave the
  *            value store untouched; v_strides as for keys (ignored when v is NULL)
  *   start, n_new  token range of every stream, start + n_new <= capacity
+ *   row_start  device int32 [B] or NULL: batch row b appends its n_new tokens at row_start[b]
+ *            instead of `start` (rows at different lengths; `start` is then ignored). Requires
+ *            both tails. Precondition row_start[b] + n_new <= capacity (a row that would pass the
+ *            capacity is left untouched).
  * Errors: NULL (also: a range that is not group-aligned without ktail, or without vtail when v is
  * given), SHAPE, ALIGN (k, v and stride*element_size not multiples of 16 bytes), CAPACITY,
  * UNSUPPORTED, HIP. n_new == 0 is a no-op.
  */
 headq_status headq_cache_append(const headq_config* cfg, const headq_cache* cache, const void* k,
                                 const int64_t k_strides[3], const void* v, const int64_t v_strides[3],
-                                int64_t start, int64_t n_new, void* stream);
+                                int64_t start, int64_t n_new, const int32_t* row_start, void* stream);
 
 /*
  * headq_decode_attn — one decode step of attention for every (b, query head) over the first
@@ -167,6 +171,9 @@ headq_status headq_cache_append(const headq_config* cfg, const headq_cache* cach
  *   q           device [B][Hq][d] in query_dtype (contiguous)
  *   n_ctx       tokens attended, 1 <= n_ctx <= capacity; the n_ctx % 32 tokens past the last
  *               whole group are read from ktail / vtail with exact keys and values (no side code)
+ *   row_len     device int32 [B] or NULL: batch row b attends its first row_len[b] tokens
+ *               (precondition 1 <= row_len[b] <= n_ctx; n_ctx then only bounds the rows, sizes
+ *               the splits and is the row stride of logits_dbg). Requires both tails.
  *   out         device [B][Hq][d] in out_dtype (HEADQ_F32 or HEADQ_BF16), contiguous
  *   corr_scale  multiplies the correction: 1 = HeadQ, 0 = base code only, -1 = wrong sign
  *   logits_dbg  device f32 [B][Hq][n_ctx] corrected logits in natural-log units, or NULL
@@ -181,7 +188,8 @@ headq_status headq_cache_append(const headq_config* cfg, const headq_cache* cach
  * UNSUPPORTED, HIP.
  */
 headq_status headq_decode_attn(const headq_config* cfg, const headq_cache* cache, const void* q,
-                               int64_t n_ctx, void* out, int32_t out_dtype, float corr_scale, float* logits_dbg,
+                               int64_t n_ctx, const int32_t* row_len, void* out, int32_t out_dtype, float corr_scale,
+                               float* logits_dbg,
                                int32_t n_splits, void* ws, size_t* ws_bytes, void* stream);
 
 /* Human-readable name of a status code (static storage). */

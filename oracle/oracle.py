@@ -251,11 +251,23 @@ def _write_groups(cache, b, h, start, k, v, U_h, value_mode, value_dtype, bits, 
     return enc
 
 
-def decode(cache, q, U, n_ctx, kappa=1.0, value_mode=0, value_dtype=1, b_range=None, want_logits=True):
+def decode(cache, q, U, n_ctx, kappa=1.0, value_mode=0, value_dtype=1, b_range=None, want_logits=True,
+           row_len=None):
     """fp64 decode attention from the packed cache.
 
     q: f32 [B][Hq][d]; U: f32 [Hkv][d][r] (or None). Returns (logits f64 [B][Hq][n_ctx] natural-log
-    units or None, out f64 [B][Hq][d]); rows outside b_range stay zero."""
+    units or None, out f64 [B][Hq][d]); rows outside b_range stay zero. row_len: optional per-row
+    token counts (each <= n_ctx); a row's logits past its length stay zero."""
+    if row_len is not None:
+        B = q.shape[0]
+        out = np.zeros((B, q.shape[1], q.shape[2]), np.float64)
+        logits = np.zeros((B, q.shape[1], n_ctx), np.float64) if want_logits else None
+        for b in range(B):
+            lg, o = decode(cache, q, U, int(row_len[b]), kappa, value_mode, value_dtype, (b, b + 1), want_logits)
+            out[b] = o[b]
+            if want_logits:
+                logits[b, :, :int(row_len[b])] = lg[b]
+        return logits, out
     kcode = np.ascontiguousarray(cache["kcode"])
     B, Hkv, cap, _ = kcode.shape
     q = np.ascontiguousarray(q, dtype=np.float32)

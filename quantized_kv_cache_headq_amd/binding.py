@@ -62,8 +62,8 @@ def load() -> ctypes.CDLL:
         L = ctypes.CDLL(str(LIB_PATH))
         P, I32, I64, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
         L.headq_calibrate.argtypes = [P, P, I64, P, P]
-        L.headq_cache_append.argtypes = [P, P, P, P, P, P, I64, I64, P]
-        L.headq_decode_attn.argtypes = [P, P, P, I64, P, I32, F, P, I32, P, P, P]
+        L.headq_cache_append.argtypes = [P, P, P, P, P, P, I64, I64, P, P]
+        L.headq_decode_attn.argtypes = [P, P, P, I64, P, P, I32, F, P, I32, P, P, P]
         L.headq_status_string.argtypes = [ctypes.c_int]
         L.headq_status_string.restype = ctypes.c_char_p
         for fn in ("headq_calibrate", "headq_cache_append", "headq_decode_attn"):
@@ -141,31 +141,35 @@ def _strides3(t):
     return (ctypes.c_int64 * 3)(t.stride(0), t.stride(1), t.stride(2))
 
 
-def headq_cache_append(cfg: Config, cache: headq_cache, k, v=None, start: int = 0, stream=None):
-    """Append k (and v) [B][Hkv][n_new][d] (torch device tensors) at token `start`: whole groups
-    are encoded, the tokens of an unfinished last group go to the dense tails."""
+def headq_cache_append(cfg: Config, cache: headq_cache, k, v=None, start: int = 0, stream=None, row_start=None):
+    """Append k (and v) [B][Hkv][n_new][d] (torch device tensors) at token `start` (or at per-row
+    positions row_start, a device int32 [B] tensor): whole groups are encoded, the tokens of an
+    unfinished last group go to the dense tails."""
     c = cfg.c()
     ks = _strides3(k)
     vs = _strides3(v) if v is not None else None
     _check(load().headq_cache_append(ctypes.byref(c), ctypes.byref(cache), _ptr(k), ks, _ptr(v), vs, start,
-                                     k.shape[2], _stream(stream)), "headq_cache_append")
+                                     k.shape[2], _ptr(row_start), _stream(stream)), "headq_cache_append")
 
 
 def decode_workspace_bytes(cfg: Config, n_ctx: int, n_splits: int = 0) -> int:
     c = cfg.c()
     nbytes = ctypes.c_size_t(0)
-    _check(load().headq_decode_attn(ctypes.byref(c), None, None, n_ctx, None, 0, 1.0, None, n_splits, None,
+    _check(load().headq_decode_attn(ctypes.byref(c), None, None, n_ctx, None, None, 0, 1.0, None, n_splits, None,
                                     ctypes.byref(nbytes), None), "headq_decode_attn(size query)")
     return nbytes.value
 
 
 def headq_decode_attn(cfg: Config, cache: headq_cache, q, n_ctx: int, out, out_dtype: int = HEADQ_F32,
-                      corr_scale: float = 1.0, logits_dbg=None, n_splits: int = 0, ws=None, stream=None):
+                      corr_scale: float = 1.0, logits_dbg=None, n_splits: int = 0, ws=None, stream=None,
+                      row_len=None):
     """One decode step: q [B][Hq][d] -> out [B][Hq][d] (torch device tensors); ws: a zero-filled device
-    buffer of at least decode_workspace_bytes(cfg, n_ctx, n_splits) bytes (calls keep it reusable)."""
+    buffer of at least decode_workspace_bytes(cfg, n_ctx, n_splits) bytes (calls keep it reusable);
+    row_len: optional device int32 [B] tokens per row (n_ctx then bounds them)."""
     c = cfg.c()
     nbytes = ctypes.c_size_t(ws.numel() * ws.element_size())
-    _check(load().headq_decode_attn(ctypes.byref(c), ctypes.byref(cache), _ptr(q), n_ctx, _ptr(out), out_dtype,
+    _check(load().headq_decode_attn(ctypes.byref(c), ctypes.byref(cache), _ptr(q), n_ctx, _ptr(row_len), _ptr(out),
+                                    out_dtype,
                                     float(corr_scale), _ptr(logits_dbg), n_splits, _ptr(ws), ctypes.byref(nbytes),
                                     _stream(stream)), "headq_decode_attn")
 
@@ -206,11 +210,11 @@ class DeviceCache:
         return headq_cache(_ptr(self.kcode), _ptr(self.kmeta), _ptr(self.scode), _ptr(self.ssc), _ptr(self.v),
                            _ptr(self.vcode), _ptr(self.vmeta), _ptr(self.U), _ptr(self.ktail), _ptr(self.vtail))
 
-    def append(self, k, v=None, start: int = 0, stream=None):
-        headq_cache_append(self.cfg, self.c(), k, v, start, stream)
+    def append(self, k, v=None, start: int = 0, stream=None, row_start=None):
+        headq_cache_append(self.cfg, self.c(), k, v, start, stream, row_start)
 
     def decode(self, q, n_ctx: int, out=None, out_dtype: int = HEADQ_F32, corr_scale: float = 1.0, logits_dbg=None,
-               n_splits: int = 0, ws=None, stream=None):
+               n_splits: int = 0, ws=None, stream=None, row_len=None):
         import torch
         if out is None:
             out = torch.empty(q.shape, dtype=torch.float32 if out_dtype == HEADQ_F32 else torch.bfloat16,
@@ -218,7 +222,8 @@ class DeviceCache:
         if ws is None:
             nb = decode_workspace_bytes(self.cfg, n_ctx, n_splits)
             ws = torch.zeros((nb + 3) // 4, dtype=torch.float32, device=q.device)
-        headq_decode_attn(self.cfg, self.c(), q, n_ctx, out, out_dtype, corr_scale, logits_dbg, n_splits, ws, stream)
+        headq_decode_attn(self.cfg, self.c(), q, n_ctx, out, out_dtype, corr_scale, logits_dbg, n_splits, ws, stream,
+                          row_len)
         return out
 
     def nbytes(self) -> int:

@@ -73,11 +73,11 @@ struct Tile {
   __device__ bool whole(int gl) const { return gl ? w1 : w0; }
 };
 
-__device__ __forceinline__ Tile tile_of(const AppendArgs& a) {
+__device__ __forceinline__ Tile tile_of(const AppendArgs& a, int64_t start) {
   Tile tl;
   tl.bh = (int64_t)blockIdx.z * a.hkv + blockIdx.y;
-  const int64_t end = a.start + a.n_new;
-  const int64_t g_first = a.start / kGroup, n_touch = (end + kGroup - 1) / kGroup - g_first;
+  const int64_t end = start + a.n_new;
+  const int64_t g_first = start / kGroup, n_touch = (end + kGroup - 1) / kGroup - g_first;
   tl.g0 = g_first + (int64_t)blockIdx.x * kGpw;
   const bool real1 = (int64_t)blockIdx.x * kGpw + 1 < n_touch;
   tl.g1 = real1 ? tl.g0 + 1 : tl.g0;
@@ -94,23 +94,23 @@ __device__ __forceinline__ int64_t row_token(const Tile& tl, int row) {
 // Address of 16 bytes at element `c` of cache token `tok`'s row for a given input: the dense
 // tail (tokens before `start`), the caller's rows (tokens in [start, end)), or nullptr (tokens
 // past `end`, which do not exist yet). `es` is the element size, `base` the caller's (b, h) row 0.
-__device__ __forceinline__ const void* row_src(const AppendArgs& a, const void* base, int64_t ts, const void* tail,
-                                               int64_t bh, int D, int es, int64_t tok, int c) {
-  if (tok < a.start) return (const char*)tail + ((bh * kGroup + tok % kGroup) * D + c) * es;
-  if (tok < a.start + a.n_new) return (const char*)base + ((tok - a.start) * ts + c) * es;
+__device__ __forceinline__ const void* row_src(const AppendArgs& a, int64_t start, const void* base, int64_t ts,
+                                               const void* tail, int64_t bh, int D, int es, int64_t tok, int c) {
+  if (tok < start) return (const char*)tail + ((bh * kGroup + tok % kGroup) * D + c) * es;
+  if (tok < start + a.n_new) return (const char*)base + ((tok - start) * ts + c) * es;
   return nullptr;
 }
 
 // Load the 64 rows of f32/bf16 input (element stride 1 along channels, token stride ts) into an
 // f32 LDS tile with row pitch P, with 128-bit loads; rows that do not exist yet read as zero.
 template <int D, int P, bool BF16>
-__device__ __forceinline__ void load_rows(float (*dst)[P], const AppendArgs& a, const void* base, int64_t ts,
-                                          const void* tail, const Tile& tl) {
+__device__ __forceinline__ void load_rows(float (*dst)[P], const AppendArgs& a, int64_t start, const void* base,
+                                          int64_t ts, const void* tail, const Tile& tl) {
   constexpr int kElem = BF16 ? 8 : 4;  // elements per 16-byte load
   constexpr int kChunks = D / kElem;   // 16-byte chunks per row
   for (int i = threadIdx.x; i < kRows * kChunks; i += kThreads) {
     const int row = i / kChunks, ch = i % kChunks;
-    const void* src = row_src(a, base, ts, tail, tl.bh, D, BF16 ? 2 : 4, row_token(tl, row), ch * kElem);
+    const void* src = row_src(a, start, base, ts, tail, tl.bh, D, BF16 ? 2 : 4, row_token(tl, row), ch * kElem);
     const uint4 w = src ? *reinterpret_cast<const uint4*>(src) : make_uint4(0u, 0u, 0u, 0u);
     const uint32_t u[4] = {w.x, w.y, w.z, w.w};
     if constexpr (BF16) {
@@ -129,11 +129,11 @@ __device__ __forceinline__ void load_rows(float (*dst)[P], const AppendArgs& a, 
 // Copy the caller's rows of the unfinished last group into the dense tails (rows t % 32).
 // Done by workgroup 0 only, after every read of the tails in this launch: the only group that
 // reads tail rows is the first touched one, which workgroup 0 owns.
-__device__ __forceinline__ void write_tails(const AppendArgs& a, int64_t bh, int D, const void* kbase, int kes,
-                                            const void* vbase, int ves) {
-  const int64_t end = a.start + a.n_new;
+__device__ __forceinline__ void write_tails(const AppendArgs& a, int64_t start, int64_t bh, int D, const void* kbase,
+                                            int kes, const void* vbase, int ves) {
+  const int64_t end = start + a.n_new;
   if (end % kGroup == 0) return;
-  const int64_t t_lo = a.start > end / kGroup * kGroup ? a.start : end / kGroup * kGroup;
+  const int64_t t_lo = start > end / kGroup * kGroup ? start : end / kGroup * kGroup;
   const int n_rows = (int)(end - t_lo);
   for (int pass = 0; pass < 2; ++pass) {
     const int es = pass ? ves : kes;
@@ -146,7 +146,7 @@ __device__ __forceinline__ void write_tails(const AppendArgs& a, int64_t bh, int
       const int64_t tok = t_lo + i / chunks;
       const int ch = i % chunks;
       *reinterpret_cast<uint4*>(tail + (bh * kGroup + tok % kGroup) * D * es + ch * 16) =
-          *reinterpret_cast<const uint4*>(src + (tok - a.start) * ts * es + ch * 16);
+          *reinterpret_cast<const uint4*>(src + (tok - start) * ts * es + ch * 16);
     }
   }
 }
@@ -166,17 +166,20 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
   __shared__ float amax_s[4][kRows];
   __shared__ float U_s[UL && R > 0 ? D * R : 1];
 
-  const Tile tl = tile_of(a);
+  const int h = blockIdx.y, b = blockIdx.z;
+  // this row's append position; a row that would pass the capacity is left untouched
+  const int64_t st = a.row_start ? (int64_t)a.row_start[b] : a.start;
+  if (st < 0 || st + a.n_new > a.cap) return;
+  const Tile tl = tile_of(a, st);
   const int tid = threadIdx.x, lane = tid % 64;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
-  const int h = blockIdx.y, b = blockIdx.z;
   const int64_t groups_cap = a.cap / kGroup;
   const int64_t gs0 = tl.bh * groups_cap;  // cache group 0 of this stream
   const char* kin = (const char*)a.k + ((int64_t)b * a.ks_b + (int64_t)h * a.ks_h) * (KBF16 ? 2 : 4);
   const int ves = a.value_bf16 ? 2 : 4;
   const char* vin = a.v ? (const char*)a.v + ((int64_t)b * a.vs_b + (int64_t)h * a.vs_h) * ves : nullptr;
   if (!tl.w0) {  // no whole group here (the second one cannot be whole either): tail rows only
-    if (blockIdx.x == 0) write_tails(a, tl.bh, D, kin, KBF16 ? 2 : 4, vin, ves);
+    if (blockIdx.x == 0) write_tails(a, st, tl.bh, D, kin, KBF16 ? 2 : 4, vin, ves);
     return;
   }
 
@@ -192,13 +195,13 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
     for (int k = 0; k < VMAX; ++k) {
       if (k < vpt) {
         const int i = tid + k * kThreads, row = i / vchunks, c0 = (i % vchunks) * vper;
-        const void* src = row_src(a, vin, a.vs_t, a.vtail, tl.bh, D, ves, row_token(tl, row), c0);
+        const void* src = row_src(a, st, vin, a.vs_t, a.vtail, tl.bh, D, ves, row_token(tl, row), c0);
         vr[k] = src ? *reinterpret_cast<const uint4*>(src) : make_uint4(0u, 0u, 0u, 0u);
       }
     }
   }
 
-  load_rows<D, P, KBF16>(ke, a, kin, a.ks_t, a.ktail, tl);
+  load_rows<D, P, KBF16>(ke, a, st, kin, a.ks_t, a.ktail, tl);
   if constexpr (UL && R > 0) {
     const float4* Ug = reinterpret_cast<const float4*>(a.U + (int64_t)h * D * R);
     for (int i = tid; i < D * R / 4; i += kThreads) reinterpret_cast<float4*>(U_s)[i] = Ug[i];
@@ -407,16 +410,17 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
   }
   }  // values
 
-  if (blockIdx.x == 0 && (a.start + a.n_new) % kGroup) {
+  if (blockIdx.x == 0 && (st + a.n_new) % kGroup) {
     __syncthreads();  // every tail row this workgroup read has been consumed
-    write_tails(a, tl.bh, D, kin, KBF16 ? 2 : 4, vin, ves);
+    write_tails(a, st, tl.bh, D, kin, KBF16 ? 2 : 4, vin, ves);
   }
 }
 
 template <int D, int R>
 hipError_t launch_dr(const AppendArgs& a, hipStream_t s) {
   const int64_t end = a.start + a.n_new;
-  const int64_t n_touch = (end + kGroup - 1) / kGroup - a.start / kGroup;  // groups the range touches
+  // groups the range touches; with per-row positions, the most any row can touch
+  const int64_t n_touch = a.row_start ? (a.n_new + kGroup - 1) / kGroup + 1 : (end + kGroup - 1) / kGroup - a.start / kGroup;
   dim3 grid((unsigned)((n_touch + kGpw - 1) / kGpw), (unsigned)a.hkv, (unsigned)a.batch);
   const bool small = (int64_t)grid.x * grid.y * grid.z <= 1024;  // at most ~4 workgroups per CU
   if (a.key_bf16) {

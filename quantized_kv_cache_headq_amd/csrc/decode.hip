@@ -83,8 +83,13 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
   for (int j = 0; j < HPT; ++j) o[j] = 0.0f;
 
   // whole groups, then (index n_groups) the unfinished group held exactly in the tails
-  const int64_t n_groups = a.n_ctx / kGroup;
-  const int tail_len = (int)(a.n_ctx % kGroup);
+  int64_t n_ctx = a.n_ctx;  // this row's attended tokens
+  if (a.row_len) {
+    const int64_t r = a.row_len[b];
+    n_ctx = r < 0 ? 0 : (r > a.n_ctx ? a.n_ctx : r);
+  }
+  const int64_t n_groups = n_ctx / kGroup;
+  const int tail_len = (int)(n_ctx % kGroup);
   const int64_t n_units = n_groups + (tail_len ? 1 : 0);
   const int64_t g_begin = (int64_t)split * a.groups_per_split;
   int64_t g_end = g_begin + a.groups_per_split;
@@ -274,7 +279,7 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(DecodeArgs a) {
     l = fmaf(ml[2 * s + 1], w, l);
     acc = fmaf(a.ws_o[(row * a.n_splits + s) * D + c], w, acc);
   }
-  const float o = acc / l;
+  const float o = l > 0.0f ? acc / l : 0.0f;  // a row without tokens reads out zeros
   if (a.out_bf16)
     ((__bf16*)a.out)[row * D + c] = (__bf16)o;
   else

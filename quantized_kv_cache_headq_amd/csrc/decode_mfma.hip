@@ -436,12 +436,13 @@ __device__ __forceinline__ void process_group(const GroupRaw<D, R, VQ2>& cur, co
 // adds p . v to its own output channels 16*ct + 4*quad + j, fetching the other quads'
 // probabilities by lane shuffles.
 template <int D>
-__device__ __forceinline__ void process_tail(const DecodeArgs& a, int64_t bh, int b, int hq0, int g, int n,
+__device__ __forceinline__ void process_tail(const DecodeArgs& a, int64_t n_ctx, int64_t bh, int b, int hq0, int g,
+                                             int n,
                                              int quad, const float (*qs)[D], float inv_scale, floatx4* o_acc,
                                              float* z_acc, int n_z, float& m_run, float& l_run) {
   constexpr int NCT = D / 16;
-  const int64_t n_full = a.n_ctx / kGroup * kGroup;
-  const int tail_len = (int)(a.n_ctx - n_full);
+  const int64_t n_full = n_ctx / kGroup * kGroup;
+  const int tail_len = (int)(n_ctx - n_full);
   // scores of rows 8*quad + j: channels in steps of 8 (one 16-byte or two 16-byte loads per row)
   float acc[8];
 #pragma unroll
@@ -590,14 +591,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     s.vmeta = s.v;
   }
   // group indices are 32-bit and wave-uniform, so every offset below stays in scalar registers
-  const int n_groups = (int)(a.n_ctx / kGroup);
+  // this row's attended tokens: whole groups, then the unfinished one from the tails
+  int64_t n_ctx = a.n_ctx;
+  if (a.row_len) {
+    const int64_t r = a.row_len[b];
+    n_ctx = r < 0 ? 0 : (r > a.n_ctx ? a.n_ctx : r);
+  }
+  const int n_groups = (int)(n_ctx / kGroup);
   const int W = a.n_splits * kWaves;
   const int rot = n_groups > 0 ? (int)((bh * 40503) % n_groups) : 0;
   auto group_at = [&](int j) { const int x = j + rot; return x >= n_groups ? x - n_groups : x; };
   const int j_begin = split * kWaves + wave;
   GroupRaw<D, R, VQ2> ga, gb;  // ping-pong register sets: one group computed while the next loads
   // the wave that takes the unfinished group requests its first groups after it (fewer live registers)
-  const bool tail_wave = a.n_ctx % kGroup && split == 0 && wave == 0;
+  const bool tail_wave = n_ctx % kGroup && split == 0 && wave == 0;
   if (!tail_wave) {
     if (j_begin < n_groups) load_group<D, R, VQ2>(ga, s, lane, n, quad, group_at(j_begin));
     if (j_begin + W < n_groups) load_group<D, R, VQ2>(gb, s, lane, n, quad, group_at(j_begin + W));
@@ -667,7 +674,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
   // ---- the unfinished last group (exact, from the tails), by one wave per stream
   if (tail_wave) {
-    process_tail<D>(a, bh, b, hq0, g, n, quad, qs, f.inv_scale, o_acc, z_acc, VQ2 ? NG : 0, m_run, l_run);
+    process_tail<D>(a, n_ctx, bh, b, hq0, g, n, quad, qs, f.inv_scale, o_acc, z_acc, VQ2 ? NG : 0, m_run, l_run);
     if (j_begin < n_groups) load_group<D, R, VQ2>(ga, s, lane, n, quad, group_at(j_begin));
     if (j_begin + W < n_groups) load_group<D, R, VQ2>(gb, s, lane, n, quad, group_at(j_begin + W));
   }
@@ -760,7 +767,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       ml_s[2 * (tid * S + sp)] = wgt;
       L = fmaf(ml_s[2 * (tid * S + sp) + 1], wgt, L);
     }
-    m_w[0][tid] = 1.0f / L;
+    m_w[0][tid] = L > 0.0f ? 1.0f / L : 0.0f;  // a row without tokens reads out zeros
   }
   __syncthreads();
   for (int i = tid; i < g * D; i += kThreads) {

@@ -78,7 +78,8 @@ extern "C" const char* headq_status_string(headq_status s) {
 
 extern "C" headq_status headq_cache_append(const headq_config* cfg, const headq_cache* cache, const void* k,
                                            const int64_t k_strides[3], const void* v, const int64_t v_strides[3],
-                                           int64_t start, int64_t n_new, void* stream) {
+                                           int64_t start, int64_t n_new, const int32_t* row_start,
+                                           void* stream) {
   headq_status st = check_config(cfg);
   if (st != HEADQ_OK) return st;
   if (!cache || !k || !k_strides) return HEADQ_ERR_NULL;
@@ -86,9 +87,9 @@ extern "C" headq_status headq_cache_append(const headq_config* cfg, const headq_
   st = check_cache(cfg, cache);
   if (st != HEADQ_OK) return st;
   if (start < 0 || n_new < 0) return HEADQ_ERR_SHAPE;
-  if (start + n_new > cfg->capacity) return HEADQ_ERR_CAPACITY;
+  if ((row_start ? 0 : start) + n_new > cfg->capacity) return HEADQ_ERR_CAPACITY;
   // a range that starts or ends inside a group goes through the dense tails
-  const bool group_aligned = start % headq::kGroup == 0 && (start + n_new) % headq::kGroup == 0;
+  const bool group_aligned = !row_start && start % headq::kGroup == 0 && (start + n_new) % headq::kGroup == 0;
   if (!group_aligned && (!cache->ktail || (v && !cache->vtail))) return HEADQ_ERR_NULL;
   const int kes = cfg->key_dtype == HEADQ_F32 ? 4 : 2;
   const int ves = cfg->value_dtype == HEADQ_F32 ? 4 : 2;
@@ -139,6 +140,7 @@ extern "C" headq_status headq_cache_append(const headq_config* cfg, const headq_
   a.U = cache->U;
   a.ktail = cache->ktail;
   a.vtail = cache->vtail;
+  a.row_start = row_start;
   hipStream_t s = (hipStream_t)stream;
   return finish(headq::launch_append(a, s), s);
 }
@@ -173,7 +175,8 @@ int auto_splits(const headq_config* c, int64_t n_groups, int chunks, bool mfma) 
 }  // namespace
 
 extern "C" headq_status headq_decode_attn(const headq_config* cfg, const headq_cache* cache, const void* q,
-                                          int64_t n_ctx, void* out, int32_t out_dtype, float corr_scale,
+                                          int64_t n_ctx, const int32_t* row_len, void* out, int32_t out_dtype,
+                                          float corr_scale,
                                           float* logits_dbg, int32_t n_splits, void* ws, size_t* ws_bytes,
                                           void* stream) {
   headq_status st = check_config(cfg);
@@ -199,7 +202,7 @@ extern "C" headq_status headq_decode_attn(const headq_config* cfg, const headq_c
   if (!cache || !q || !out) return HEADQ_ERR_NULL;
   st = check_cache(cfg, cache);
   if (st != HEADQ_OK) return st;
-  if (n_ctx % headq::kGroup && (!cache->ktail || !cache->vtail)) return HEADQ_ERR_NULL;
+  if ((row_len || n_ctx % headq::kGroup) && (!cache->ktail || !cache->vtail)) return HEADQ_ERR_NULL;
   if (*ws_bytes < need) return HEADQ_ERR_WORKSPACE;
   if (!aligned16(q) || !aligned16(out) || !aligned16(ws) || (logits_dbg && !aligned16(logits_dbg)))
     return HEADQ_ERR_ALIGN;
@@ -234,6 +237,7 @@ extern "C" headq_status headq_decode_attn(const headq_config* cfg, const headq_c
   a.ktail = cache->ktail;
   a.vtail = cache->vtail;
   a.key_bf16 = cfg->key_dtype == HEADQ_BF16;
+  a.row_len = row_len;
   a.logits_dbg = logits_dbg;
   a.ws_count = (uint32_t*)ws;
   a.ws_o = (float*)((char*)ws + headq::decode_ws_counter_bytes(cfg->batch, cfg->n_kv_heads));

@@ -47,6 +47,7 @@ struct AppendArgs {
   const float* U;
   void* ktail;                 // [B][Hkv][32][d] key_dtype: tokens of the unfinished last group
   void* vtail;                 // [B][Hkv][32][d] value_dtype
+  const int32_t* row_start;    // [B] per-row append position, or null (all rows at `start`)
 };
 
 struct DecodeArgs {
@@ -70,6 +71,7 @@ struct DecodeArgs {
   const void* ktail;           // tail of the unfinished group (n_ctx % 32 tokens), exact
   const void* vtail;
   int key_bf16;                // dtype of ktail
+  const int32_t* row_len;      // [B] per-row attended tokens (<= n_ctx), or null (all n_ctx)
   float* logits_dbg;           // may be null
   uint32_t* ws_count;          // [B][Hkv] arrival counters (zero between calls)
   float* ws_o;                 // [B][Hq][S][d]

@@ -92,3 +92,45 @@ def test_context_inside_the_tail_only():
 def test_tail_with_splits(splits):
     w = synth.scaled(W["qwen7b_decode"], n_q_heads=14, n_kv_heads=2, rank=32)
     _run(w, 1, 640, [(0, 512), (512, 17)], {529}, n_splits=splits)
+
+
+def test_ragged_rows_per_row_positions_and_lengths():
+    """Rows at different lengths: appends at per-row positions (device row_start), decode of
+    per-row lengths (device row_len), against the oracle fed row by row."""
+    import torch
+    import quantized_kv_cache_headq_amd as hq
+    from .gpu_helpers import config, to_device
+    w = synth.scaled(W["qwen7b_decode"], n_q_heads=14, n_kv_heads=2)
+    B, cap = 3, 192
+    say("ragged", w.name, f"B={B} cap={cap}")
+    U = orc.calibrate(synth.calibration_queries(w, n_cal=128), w.n_kv_heads, w.rank)[0]
+    Kf = synth.stack_streams(w, "keys", B, cap)
+    Vf = synth.stack_streams(w, "values", B, cap)
+    dc = hq.DeviceCache(config(w, B, cap))
+    dc.set_basis(U)
+    oc = orc.empty_cache(B, w.n_kv_heads, cap, w.head_dim, w.rank, VMODE[w.value_mode], VDT[w.value_dtype],
+                         key_dtype=VDT[w.key_dtype])
+    lengths = np.array([0, 3, 7])  # rows 1 and 2 start inside group 0 (earlier rows read as zeros)
+    for n_new in (33, 1, 1, 40, 24, 1):
+        K = np.stack([Kf[b, :, lengths[b]:lengths[b] + n_new] for b in range(B)])
+        V = np.stack([Vf[b, :, lengths[b]:lengths[b] + n_new] for b in range(B)])
+        rs = torch.tensor(lengths, dtype=torch.int32, device="cuda")
+        dc.append(to_device(K, w.key_dtype), to_device(V, w.value_dtype), 0, row_start=rs)
+        for b in range(B):
+            for h in range(w.n_kv_heads):
+                orc.write_stream(oc, b, h, int(lengths[b]), K[b, h], value_payload(V[b, h], w), U[h],
+                                 VMODE[w.value_mode], VDT[w.value_dtype])
+        lengths = lengths + n_new
+        compare_cache(dc, oc)
+        n_max = int(lengths.max())
+        q = synth.decode_queries(w, position=n_max, batch=B)
+        rl = torch.tensor(lengths, dtype=torch.int32, device="cuda")
+        qd = to_device(q, w.query_dtype)
+        lg = torch.full((B, w.n_q_heads, n_max), float("nan"), device="cuda")
+        out = dc.decode(qd, n_max, logits_dbg=lg, row_len=rl)
+        torch.cuda.synchronize()
+        ref_l, ref_o = orc.decode(oc, q, U, n_max, 1.0, VMODE[w.value_mode], VDT[w.value_dtype], row_len=lengths)
+        lg = lg.cpu().numpy()
+        for b in range(B):
+            check_logits(lg[b, :, :lengths[b]], ref_l[b, :, :lengths[b]])
+        check_out(out.float().cpu().numpy(), ref_o, False)

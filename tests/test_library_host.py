@@ -106,7 +106,7 @@ class _FakeDev:
         return self._strides if i is None else self._strides[i]
 
 
-def _append_status(cfg, cache, k, v=None, start=0, n_new=None):
+def _append_status(cfg, cache, k, v=None, start=0, n_new=None, row_start=None):
     lib = hq.load()
     c = cfg.c()
     ks = (ctypes.c_int64 * 3)(*k._strides[:3]) if k is not None else None
@@ -114,7 +114,7 @@ def _append_status(cfg, cache, k, v=None, start=0, n_new=None):
     n = k.shape[2] if n_new is None else n_new
     return lib.headq_cache_append(ctypes.byref(c), ctypes.byref(cache) if cache is not None else None,
                                   k.addr if k is not None else None, ks, v.addr if v is not None else None, vs,
-                                  start, n, None)
+                                  start, n, row_start, None)
 
 
 def _fake_cache(cfg):
@@ -141,6 +141,7 @@ def test_append_validation_statuses():
     assert _append_status(_cfg(capacity=100), cache, k) == 3                  # capacity % 32
     assert _append_status(cfg, cache, k, start=16) == 1                       # inside a group, no tails
     assert _append_status(cfg, cache, k, n_new=48) == 1                       # ends inside a group, no tails
+    assert _append_status(cfg, cache, k, row_start=0x60000000) == 1           # per-row positions need tails
     assert _append_status(cfg, cache, k, start=96) == 4                       # start + n > cap
     assert _append_status(cfg, cache, _fake_keys(cfg, align=4)) == 3          # misaligned keys
     bad = bd.headq_cache(0x10000004, 0x10001000, 0x10002000, 0x10003000, 0x10004000, 0, 0, 0x10007000)
@@ -154,13 +155,13 @@ def test_append_validation_statuses():
 
 
 def _decode_status(cfg, cache=None, q=0x30000000, n_ctx=64, out=0x40000000, ws=0x50000000, nbytes=1 << 20,
-                   n_splits=0, out_dtype=0):
+                   n_splits=0, out_dtype=0, row_len=None):
     lib = hq.load()
     c = cfg.c()
     nb = ctypes.c_size_t(nbytes)
     cache = _fake_cache(cfg) if cache is None else cache
-    st = lib.headq_decode_attn(ctypes.byref(c), ctypes.byref(cache), q, n_ctx, out, out_dtype, 1.0, None, n_splits,
-                               ws, ctypes.byref(nb), None)
+    st = lib.headq_decode_attn(ctypes.byref(c), ctypes.byref(cache), q, n_ctx, row_len, out, out_dtype, 1.0, None,
+                               n_splits, ws, ctypes.byref(nb), None)
     return st, nb.value
 
 
@@ -176,6 +177,7 @@ def test_decode_workspace_query_and_validation():
     assert _decode_status(cfg, n_ctx=0)[0] == 2
     assert _decode_status(cfg, n_splits=3)[0] == 2                            # more splits than groups
     assert _decode_status(cfg, n_ctx=48, n_splits=3)[0] == 2                  # 1 whole group + the tail
+    assert _decode_status(cfg, row_len=0x60000000)[0] == 1                    # per-row lengths need tails
     assert _decode_status(cfg, q=0x30000002)[0] == 3                          # misaligned query
     assert _decode_status(cfg, out_dtype=5)[0] == 7
     assert _decode_status(cfg, q=None)[0] == 1
