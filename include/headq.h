@@ -50,6 +50,12 @@
  *                                        row 0 = step, row 1 = zero, token index fastest
  *   ktail  key_dtype   [B][Hkv][G][d]    tokens of the unfinished last group (row t % 32), exact
  *   vtail  value_dtype [B][Hkv][G][d]    their values, exact (also in 2-bit mode)
+ * Paged caches (block_table != NULL): every array above except U and the tails is instead a pool
+ * of n_pages pages, the [B][Hkv][cap/G] group index replaced by [n_pages][Hkv]: the group g of
+ * batch row b lives in page block_table[b * max_pages + g] (one page = one 32-token group of all
+ * KV heads; e.g. kcode [n_pages][Hkv][G][d/4], v [n_pages][Hkv][d][G]); `capacity` is then the
+ * per-row logical capacity, at most 32 * max_pages. Pages are assigned by the caller; entries
+ * outside [0, n_pages) are clamped by the kernels (to stay inside the pools).
  *   U      f32  [Hkv][d][r]              the side basis (device copy of headq_calibrate's output)
  */
 #ifndef HEADQ_H
@@ -109,6 +115,9 @@ typedef struct headq_cache { /* device pointers, layouts in the header comment a
   const float* U;  /* [Hkv][d][r]; may be NULL when rank == 0 */
   void* ktail;     /* dense tail keys; may be NULL if every append and n_ctx is group-aligned */
   void* vtail;     /* dense tail values; may be NULL likewise */
+  const int32_t* block_table; /* device int32 [B][max_pages]: paged cache, or NULL (contiguous) */
+  int64_t max_pages;          /* pages per batch row in block_table */
+  int64_t n_pages;            /* pages in each pool */
 } headq_cache;
 
 /*
@@ -217,6 +226,16 @@ static inline size_t headq_vcode_bytes(const headq_config* c) {
 static inline size_t headq_vmeta_bytes(const headq_config* c) {
   return (size_t)c->batch * c->n_kv_heads * c->capacity * (c->head_dim / 32) * 2 * 2;
 }
+/* Paged pools: bytes of one page (one 32-token group of every KV head) of each array. */
+static inline size_t headq_page_kcode_bytes(const headq_config* c) { return (size_t)c->n_kv_heads * 32 * (c->head_dim / 4); }
+static inline size_t headq_page_kmeta_bytes(const headq_config* c) { return (size_t)c->n_kv_heads * 2 * c->head_dim * 2; }
+static inline size_t headq_page_scode_bytes(const headq_config* c) { return (size_t)c->n_kv_heads * 32 * (c->rank / 2); }
+static inline size_t headq_page_ssc_bytes(const headq_config* c) { return (size_t)c->n_kv_heads * 32 * 2; }
+static inline size_t headq_page_v_bytes(const headq_config* c) {
+  return (size_t)c->n_kv_heads * 32 * c->head_dim * (c->value_dtype == HEADQ_F32 ? 4 : 2);
+}
+static inline size_t headq_page_vcode_bytes(const headq_config* c) { return (size_t)c->n_kv_heads * c->head_dim * 8; }
+static inline size_t headq_page_vmeta_bytes(const headq_config* c) { return (size_t)c->n_kv_heads * 2 * c->head_dim * 2; }
 static inline size_t headq_ktail_bytes(const headq_config* c) {
   return (size_t)c->batch * c->n_kv_heads * 32 * c->head_dim * (c->key_dtype == HEADQ_F32 ? 4 : 2);
 }

@@ -4,7 +4,7 @@ The compute lives in libheadq.so (hand-written HIP kernels behind a C ABI declar
 include/headq.h); this package only marshals arguments to it.
 """
 from .binding import (EXPORTS, HEADQ_BF16, HEADQ_F32, HEADQ_V_DENSE, HEADQ_V_Q2, Config, DeviceCache, HeadQError,
-                      decode_workspace_bytes, headq_cache_append, headq_calibrate, headq_decode_attn, load)
+                      PagedDeviceCache, decode_workspace_bytes, headq_cache_append, headq_calibrate, headq_decode_attn, load)
 
 __all__ = ["EXPORTS", "HEADQ_BF16", "HEADQ_F32", "HEADQ_V_DENSE", "HEADQ_V_Q2", "Config", "DeviceCache", "HeadQError",
-           "decode_workspace_bytes", "headq_cache_append", "headq_calibrate", "headq_decode_attn", "load"]
+           "PagedDeviceCache", "decode_workspace_bytes", "headq_cache_append", "headq_calibrate", "headq_decode_attn", "load"]

@@ -47,6 +47,7 @@ class headq_cache(ctypes.Structure):
         ("kcode", ctypes.c_void_p), ("kmeta", ctypes.c_void_p), ("scode", ctypes.c_void_p),
         ("ssc", ctypes.c_void_p), ("v", ctypes.c_void_p), ("vcode", ctypes.c_void_p),
         ("vmeta", ctypes.c_void_p), ("U", ctypes.c_void_p), ("ktail", ctypes.c_void_p), ("vtail", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p), ("max_pages", ctypes.c_int64), ("n_pages", ctypes.c_int64),
     ]
 
 
@@ -208,7 +209,8 @@ class DeviceCache:
 
     def c(self) -> headq_cache:
         return headq_cache(_ptr(self.kcode), _ptr(self.kmeta), _ptr(self.scode), _ptr(self.ssc), _ptr(self.v),
-                           _ptr(self.vcode), _ptr(self.vmeta), _ptr(self.U), _ptr(self.ktail), _ptr(self.vtail))
+                           _ptr(self.vcode), _ptr(self.vmeta), _ptr(self.U), _ptr(self.ktail), _ptr(self.vtail),
+                           None, 0, 0)
 
     def append(self, k, v=None, start: int = 0, stream=None, row_start=None):
         headq_cache_append(self.cfg, self.c(), k, v, start, stream, row_start)
@@ -230,3 +232,41 @@ class DeviceCache:
         return sum(t.numel() * t.element_size() for t in (self.kcode, self.kmeta, self.scode, self.ssc, self.v,
                                                            self.vcode, self.vmeta, self.ktail, self.vtail)
                    if t is not None)
+
+
+class PagedDeviceCache(DeviceCache):
+    """A paged cache: every packed array is a pool of n_pages pages (one page = one 32-token group
+    of all KV heads), and group g of batch row b lives in page block_table[b][g]. The tails stay per
+    row. block_table is a device int32 [B][max_pages] tensor the caller fills (and may change
+    between calls); cfg.capacity is the per-row logical capacity, at most 32 * max_pages."""
+
+    def __init__(self, cfg: Config, n_pages: int, max_pages: int, device="cuda"):
+        import torch
+        if cfg.capacity > GROUP * max_pages:
+            raise ValueError("capacity exceeds 32 * max_pages")
+        self.cfg = cfg
+        self.n_pages, self.max_pages = n_pages, max_pages
+        H, d, r, P = cfg.n_kv_heads, cfg.head_dim, cfg.rank, n_pages
+        u8, i16 = torch.uint8, torch.int16
+        self.kcode = torch.zeros((P, H, GROUP, d // 4), dtype=u8, device=device)
+        self.kmeta = torch.zeros((P, H, 2, d), dtype=i16, device=device)
+        self.scode = torch.zeros((P, H, GROUP, max(r // 2, 1)), dtype=u8, device=device) if r else None
+        self.ssc = torch.zeros((P, H, GROUP), dtype=i16, device=device) if r else None
+        self.v = self.vcode = self.vmeta = None
+        if cfg.value_mode == HEADQ_V_DENSE:
+            vdt = torch.float32 if cfg.value_dtype == HEADQ_F32 else torch.bfloat16
+            self.v = torch.zeros((P, H, d, GROUP), dtype=vdt, device=device)
+        else:
+            self.vcode = torch.zeros((P, H, d * 8), dtype=u8, device=device)
+            self.vmeta = torch.zeros((P, H, 2, d // GROUP, GROUP), dtype=i16, device=device)
+        kdt = torch.float32 if cfg.key_dtype == HEADQ_F32 else torch.bfloat16
+        vdt = torch.float32 if cfg.value_dtype == HEADQ_F32 else torch.bfloat16
+        self.ktail = torch.zeros((cfg.batch, H, GROUP, d), dtype=kdt, device=device)
+        self.vtail = torch.zeros((cfg.batch, H, GROUP, d), dtype=vdt, device=device)
+        self.block_table = torch.zeros((cfg.batch, max_pages), dtype=torch.int32, device=device)
+        self.U = None
+
+    def c(self) -> headq_cache:
+        return headq_cache(_ptr(self.kcode), _ptr(self.kmeta), _ptr(self.scode), _ptr(self.ssc), _ptr(self.v),
+                           _ptr(self.vcode), _ptr(self.vmeta), _ptr(self.U), _ptr(self.ktail), _ptr(self.vtail),
+                           _ptr(self.block_table), self.max_pages, self.n_pages)

@@ -173,8 +173,6 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
   const Tile tl = tile_of(a, st);
   const int tid = threadIdx.x, lane = tid % 64;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
-  const int64_t groups_cap = a.cap / kGroup;
-  const int64_t gs0 = tl.bh * groups_cap;  // cache group 0 of this stream
   const char* kin = (const char*)a.k + ((int64_t)b * a.ks_b + (int64_t)h * a.ks_h) * (KBF16 ? 2 : 4);
   const int ves = a.value_bf16 ? 2 : 4;
   const char* vin = a.v ? (const char*)a.v + ((int64_t)b * a.vs_b + (int64_t)h * a.vs_h) * ves : nullptr;
@@ -221,7 +219,7 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
     uint16_t sb, zb;
     minmax_step_zero(lo, hi, 3.0f, s, z, inv, sb, zb);
     if (tl.whole(gl)) {
-      uint16_t* meta = a.kmeta + (gs0 + tl.group(gl)) * 2 * D;
+      uint16_t* meta = a.kmeta + a.map.block(b, h, tl.group(gl)) * 2 * D;
       meta[c] = sb;
       meta[D + c] = zb;
     }
@@ -245,7 +243,7 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
     }
     if (tl.whole(gl)) {
       const int64_t tok = row_token(tl, row);
-      *reinterpret_cast<uint32_t*>(a.kcode + (tl.bh * a.cap + tok) * (D / 4) + c0 / 4) = word;
+      *reinterpret_cast<uint32_t*>(a.kcode + a.map.row(b, h, tok) * (D / 4) + c0 / 4) = word;
     }
   }
 
@@ -302,14 +300,15 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
       }
       if (tl.whole(gl)) {
         const int64_t tok = row_token(tl, row);
-        uint8_t* dst = a.scode + (tl.bh * a.cap + tok) * (R / 2) + wave * (CW / 2);
+        const int64_t trow = a.map.row(b, h, tok);
+        uint8_t* dst = a.scode + trow * (R / 2) + wave * (CW / 2);
         if constexpr (CW == 8)
           *reinterpret_cast<uint32_t*>(dst) = packed;
         else if constexpr (CW == 4)
           *reinterpret_cast<uint16_t*>(dst) = (uint16_t)packed;
         else
           *dst = (uint8_t)packed;
-        if (wave == 0) a.ssc[tl.bh * a.cap + tok] = sg_bits;
+        if (wave == 0) a.ssc[trow] = sg_bits;
       }
     }
   }
@@ -340,7 +339,7 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
     for (int i = tid; i < kRows * D; i += kThreads) {
       const int gl = i / (D * kGroup), c = (i / kGroup) % D, t = i % kGroup;
       if (!tl.whole(gl)) continue;
-      const int64_t idx = ((gs0 + tl.group(gl)) * D + c) * kGroup + t;
+      const int64_t idx = (a.map.block(b, h, tl.group(gl)) * D + c) * kGroup + t;
       const uint32_t x = raw[gl * kGroup + t][c];
       if (vbf)
         ((uint16_t*)a.vdense)[idx] = (uint16_t)x;
@@ -380,7 +379,7 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
       uint16_t sb, zb;
       minmax_step_zero(lo, hi, 3.0f, s, z, inv, sb, zb);
       if (tl.whole(gl)) {
-        const int64_t gabs = gs0 + tl.group(gl);
+        const int64_t gabs = a.map.block(b, h, tl.group(gl));
         a.vmeta[(gabs * 2 + 0) * NG * kGroup + gc * kGroup + t] = sb;
         a.vmeta[(gabs * 2 + 1) * NG * kGroup + gc * kGroup + t] = zb;
       }
@@ -405,7 +404,7 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
           const int row = gl * kGroup + t0 + 4 * q + e;
           v |= base_code(ke[row][c], z_s[row * NG + gc], inv_s[row * NG + gc]) << (4 * e + 2 * q);
         }
-      if (tl.whole(gl)) a.vcode[(gs0 + tl.group(gl)) * D * 8 + byte] = (uint8_t)v;
+      if (tl.whole(gl)) a.vcode[a.map.block(b, h, tl.group(gl)) * D * 8 + byte] = (uint8_t)v;
     }
   }
   }  // values

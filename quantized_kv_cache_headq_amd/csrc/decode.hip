@@ -115,7 +115,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
         sc[hh][t] = acc;
       }
     } else if (tid < D) {
-      const uint16_t* meta = a.kmeta + (bh * (a.cap / kGroup) + gi) * 2 * D;
+      const uint16_t* meta = a.kmeta + a.map.block(b, h, gi) * 2 * D;
       sz[0][tid] = f16_bits_to_f32(meta[tid]);
       sz[1][tid] = f16_bits_to_f32(meta[D + tid]);
     }
@@ -125,15 +125,16 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
     if (!is_tail) {
       const int t = tid / 8, sub = tid % 8;
       const int64_t tok = gi * kGroup + t;
-      const uint32_t* kc = (const uint32_t*)(a.kcode + (bh * a.cap + tok) * (D / 4));
+      const int64_t trow = a.map.row(b, h, tok);
+      const uint32_t* kc = (const uint32_t*)(a.kcode + trow * (D / 4));
       uint32_t words[D / 16];
 #pragma unroll
       for (int w = 0; w < D / 16; ++w) words[w] = kc[w];
       float sg = 0.0f;
       uint32_t sw[RU / 8 > 0 ? RU / 8 : 1];
       if constexpr (R > 0) {
-        sg = f16_bits_to_f32(a.ssc[bh * a.cap + tok]);
-        const uint8_t* sp = a.scode + (bh * a.cap + tok) * (R / 2);
+        sg = f16_bits_to_f32(a.ssc[trow]);
+        const uint8_t* sp = a.scode + trow * (R / 2);
         if constexpr (R >= 8) {
 #pragma unroll
           for (int w = 0; w < R / 8; ++w) sw[w] = ((const uint32_t*)sp)[w];
@@ -189,7 +190,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
     // C: o = o * alpha + p . V
     {
       float v[kGroup];
-      const int64_t gabs = bh * (a.cap / kGroup) + gi;
+      const int64_t gabs = is_tail ? 0 : a.map.block(b, h, gi);
       if (is_tail) {
         // exact tail values, zero past n_ctx (their probabilities are 0)
 #pragma unroll

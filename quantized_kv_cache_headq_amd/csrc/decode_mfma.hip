@@ -202,12 +202,33 @@ struct GroupRaw {
 };
 
 template <int D, int R, bool VQ2>
-__device__ __forceinline__ void load_group(GroupRaw<D, R, VQ2>& g, const Stream& s, int lane, int n, int quad,
-                                           int gi_in) {
+__device__ __forceinline__ void load_group(GroupRaw<D, R, VQ2>& g, const Stream& s_stream, const DecodeArgs& a, int b,
+                                           int h, int lane, int n, int quad, int gi_in) {
   using KS = KSide<D, R, VQ2>;
   // the group index is wave-uniform; saying so keeps every group offset in a scalar register
   // (a per-lane offset would make the compiler loop over the lanes around each buffer load)
-  const int gi = __builtin_amdgcn_readfirstlane(gi_in);
+  int gi = __builtin_amdgcn_readfirstlane(gi_in);
+  Stream s = s_stream;
+  if (a.map.block_table) {
+    // paged cache: this group's block in the pools, one buffer resource per array from its own
+    // 64-bit base (pools may exceed the 32-bit offset range of a single resource)
+    int64_t page = __builtin_amdgcn_readfirstlane(a.map.block_table[(int64_t)b * a.map.max_pages + gi]);
+    page = page < 0 ? 0 : (page >= a.map.n_pages ? a.map.n_pages - 1 : page);
+    const int64_t blk = page * a.hkv + h;
+    s.kcode = make_rsrc(a.kcode + blk * KS::KC, KS::KC);
+    s.kmeta = make_rsrc(a.kmeta + blk * 2 * D, KS::KM);
+    if constexpr (R > 0) {
+      s.scode = make_rsrc(a.scode + blk * KS::SC, KS::SC);
+      s.ssc = make_rsrc(a.ssc + blk * kGroup, KS::SG);
+    }
+    if constexpr (VQ2) {
+      s.v = make_rsrc(a.vcode + blk * (D * 8), D * 8);
+      s.vmeta = make_rsrc(a.vmeta + blk * 2 * D, 4 * D);
+    } else {
+      s.v = make_rsrc((const uint16_t*)a.vdense + blk * D * kGroup, D * kGroup * 2);
+    }
+    gi = 0;
+  }
   g.kc = load_piece<D / 8>(s.kcode, lane * (D / 8), gi * KS::KC);
   g.km = load_piece<D / 16>(s.kmeta, lane * (D / 16), gi * KS::KM);
   if constexpr (R > 0) {
@@ -606,8 +627,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // the wave that takes the unfinished group requests its first groups after it (fewer live registers)
   const bool tail_wave = n_ctx % kGroup && split == 0 && wave == 0;
   if (!tail_wave) {
-    if (j_begin < n_groups) load_group<D, R, VQ2>(ga, s, lane, n, quad, group_at(j_begin));
-    if (j_begin + W < n_groups) load_group<D, R, VQ2>(gb, s, lane, n, quad, group_at(j_begin + W));
+    if (j_begin < n_groups) load_group<D, R, VQ2>(ga, s, a, b, h, lane, n, quad, group_at(j_begin));
+    if (j_begin + W < n_groups) load_group<D, R, VQ2>(gb, s, a, b, h, lane, n, quad, group_at(j_begin + W));
   }
   __syncthreads();
 
@@ -675,8 +696,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // ---- the unfinished last group (exact, from the tails), by one wave per stream
   if (tail_wave) {
     process_tail<D>(a, n_ctx, bh, b, hq0, g, n, quad, qs, f.inv_scale, o_acc, z_acc, VQ2 ? NG : 0, m_run, l_run);
-    if (j_begin < n_groups) load_group<D, R, VQ2>(ga, s, lane, n, quad, group_at(j_begin));
-    if (j_begin + W < n_groups) load_group<D, R, VQ2>(gb, s, lane, n, quad, group_at(j_begin + W));
+    if (j_begin < n_groups) load_group<D, R, VQ2>(ga, s, a, b, h, lane, n, quad, group_at(j_begin));
+    if (j_begin + W < n_groups) load_group<D, R, VQ2>(gb, s, a, b, h, lane, n, quad, group_at(j_begin + W));
   }
 
   // ---- this wave's groups
@@ -684,10 +705,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   for (int j = j_begin; j < n_groups; j += 2 * W) {
     process_group<D, R, VQ2>(ga, f, slot, a, group_at(j), b, hq0, g, lane, n, quad, o_acc, z_acc, m_run, l_run);
     if (j + W >= n_groups) break;
-    if (j + 2 * W < n_groups) load_group<D, R, VQ2>(ga, s, lane, n, quad, group_at(j + 2 * W));
+    if (j + 2 * W < n_groups) load_group<D, R, VQ2>(ga, s, a, b, h, lane, n, quad, group_at(j + 2 * W));
     process_group<D, R, VQ2>(gb, f, slot, a, group_at(j + W), b, hq0, g, lane, n, quad, o_acc, z_acc, m_run,
                              l_run);
-    if (j + 3 * W < n_groups) load_group<D, R, VQ2>(gb, s, lane, n, quad, group_at(j + 3 * W));
+    if (j + 3 * W < n_groups) load_group<D, R, VQ2>(gb, s, a, b, h, lane, n, quad, group_at(j + 3 * W));
   }
   if constexpr (VQ2) {
     // zero part of the 2-bit values: sum over the four token quads, added to every channel of

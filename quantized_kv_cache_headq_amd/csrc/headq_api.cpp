@@ -50,13 +50,26 @@ headq_status check_config(const headq_config* c) {
 
 headq_status check_cache(const headq_config* c, const headq_cache* k) {
   if (!k || !k->kcode || !k->kmeta) return HEADQ_ERR_NULL;
+  if (k->block_table && (k->max_pages < 1 || k->n_pages < 1 || c->capacity > 32 * k->max_pages))
+    return HEADQ_ERR_SHAPE;
   if (c->rank > 0 && (!k->scode || !k->ssc || !k->U)) return HEADQ_ERR_NULL;
   if (c->value_mode == HEADQ_V_DENSE && !k->v) return HEADQ_ERR_NULL;
   if (c->value_mode == HEADQ_V_Q2 && (!k->vcode || !k->vmeta)) return HEADQ_ERR_NULL;
-  const void* ptrs[] = {k->kcode, k->kmeta, k->scode, k->ssc, k->v, k->vcode, k->vmeta, k->U, k->ktail, k->vtail};
+  const void* ptrs[] = {k->kcode, k->kmeta, k->scode, k->ssc, k->v, k->vcode, k->vmeta, k->U, k->ktail, k->vtail,
+                        k->block_table};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return HEADQ_ERR_ALIGN;
   return HEADQ_OK;
+}
+
+headq::CacheMap map_of(const headq_config* c, const headq_cache* k) {
+  headq::CacheMap m{};
+  m.block_table = k->block_table;
+  m.max_pages = k->max_pages;
+  m.n_pages = k->n_pages;
+  m.hkv = c->n_kv_heads;
+  m.groups_cap = c->capacity / headq::kGroup;
+  return m;
 }
 
 }  // namespace
@@ -141,6 +154,7 @@ extern "C" headq_status headq_cache_append(const headq_config* cfg, const headq_
   a.ktail = cache->ktail;
   a.vtail = cache->vtail;
   a.row_start = row_start;
+  a.map = map_of(cfg, cache);
   hipStream_t s = (hipStream_t)stream;
   return finish(headq::launch_append(a, s), s);
 }
@@ -238,6 +252,7 @@ extern "C" headq_status headq_decode_attn(const headq_config* cfg, const headq_c
   a.vtail = cache->vtail;
   a.key_bf16 = cfg->key_dtype == HEADQ_BF16;
   a.row_len = row_len;
+  a.map = map_of(cfg, cache);
   a.logits_dbg = logits_dbg;
   a.ws_count = (uint32_t*)ws;
   a.ws_o = (float*)((char*)ws + headq::decode_ws_counter_bytes(cfg->batch, cfg->n_kv_heads));

@@ -28,6 +28,30 @@ __host__ __device__ constexpr int vcode_pair_bit(int t) {  // bit of token t ins
   return 8 * (((t % 8) % 4) / 2) + 4 * (t % 2) + 2 * ((t % 8) / 4);
 }
 
+// Where the block of one (batch row b, KV head h, 32-token group g) lives. Every cache array is a
+// sequence of such blocks (kcode 32*d/4 bytes, kmeta 2*d halves, scode 32*r/2 bytes, ssc 32 halves,
+// dense values d*32 elements, vcode d*8 bytes, vmeta 2*d halves; per-token rows of kcode, scode
+// and ssc are block*32 + t). Contiguous caches: block = (b*Hkv + h)*groups_cap + g. Paged caches
+// (block_table != null): block = page*Hkv + h with page = block_table[b*max_pages + g], from pools
+// shared by all rows; an entry outside [0, n_pages) is clamped so a bad table cannot address
+// outside the pools.
+struct CacheMap {
+  const int32_t* block_table;
+  int64_t max_pages;
+  int64_t n_pages;
+  int hkv;
+  int64_t groups_cap;
+  __device__ __forceinline__ int64_t block(int b, int h, int64_t g) const {
+    if (!block_table) return ((int64_t)b * hkv + h) * groups_cap + g;
+    int64_t page = block_table[(int64_t)b * max_pages + g];
+    page = page < 0 ? 0 : (page >= n_pages ? n_pages - 1 : page);
+    return page * hkv + h;
+  }
+  __device__ __forceinline__ int64_t row(int b, int h, int64_t tok) const {
+    return block(b, h, tok / 32) * 32 + tok % 32;
+  }
+};
+
 struct AppendArgs {
   int d, r, hkv, batch;
   int64_t cap;                 // tokens per stream in the cache
@@ -48,6 +72,7 @@ struct AppendArgs {
   void* ktail;                 // [B][Hkv][32][d] key_dtype: tokens of the unfinished last group
   void* vtail;                 // [B][Hkv][32][d] value_dtype
   const int32_t* row_start;    // [B] per-row append position, or null (all rows at `start`)
+  CacheMap map;
 };
 
 struct DecodeArgs {
@@ -72,6 +97,7 @@ struct DecodeArgs {
   const void* vtail;
   int key_bf16;                // dtype of ktail
   const int32_t* row_len;      // [B] per-row attended tokens (<= n_ctx), or null (all n_ctx)
+  CacheMap map;
   float* logits_dbg;           // may be null
   uint32_t* ws_count;          // [B][Hkv] arrival counters (zero between calls)
   float* ws_o;                 // [B][Hq][S][d]

@@ -154,6 +154,24 @@ def test_append_validation_statuses():
                                                0x10007000), k) == 1          # 2-bit values need vcode/vmeta
 
 
+def _paged(cfg, max_pages, n_pages, table=0x70000000):
+    c = _fake_cache(cfg)
+    c.ktail, c.vtail = 0x11000000, 0x12000000
+    c.block_table, c.max_pages, c.n_pages = table, max_pages, n_pages
+    return c
+
+
+def test_paged_cache_validation_statuses():
+    cfg = _cfg()  # capacity 128 = 4 groups per row
+    k = _fake_keys(cfg)
+    assert _append_status(cfg, _paged(cfg, 0, 8), k) == 2                    # no table columns
+    assert _append_status(cfg, _paged(cfg, 4, 0), k) == 2                    # empty pools
+    assert _append_status(cfg, _paged(cfg, 3, 8), k) == 2                    # capacity > 32 * max_pages
+    assert _append_status(cfg, _paged(cfg, 4, 8, table=0x70000002), k) == 3  # misaligned table
+    assert _decode_status(cfg, cache=_paged(cfg, 3, 8))[0] == 2
+    assert _decode_status(cfg, cache=_paged(cfg, 4, 8, table=0x70000002))[0] == 3
+
+
 def _decode_status(cfg, cache=None, q=0x30000000, n_ctx=64, out=0x40000000, ws=0x50000000, nbytes=1 << 20,
                    n_splits=0, out_dtype=0, row_len=None):
     lib = hq.load()
