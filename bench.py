@@ -146,6 +146,8 @@ def main():
     ap.add_argument("--splits", type=int, default=0, help="token splits per stream (0 = library choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=32)
+    ap.add_argument("--paged", action="store_true",
+                    help="paged caches: every 32-token group in a page of shared pools, through a shuffled block table")
     ap.add_argument("--copy-probe", action="store_true", help="launch one 1 GiB device copy (counter scaling)")
     args = ap.parse_args()
 
@@ -187,8 +189,14 @@ def main():
     n_layers = w.layers
     caches = []
     n_copies = max(args.copies, n_layers, 4 if append_only else 1)
-    for _ in range(n_copies):
-        dc = hq.DeviceCache(cfg, device=dev)
+    G = w.n_ctx // 32
+    for i in range(n_copies):
+        if args.paged:
+            dc = hq.PagedDeviceCache(cfg, n_pages=w.batch * G, max_pages=G, device=dev)
+            perm = np.random.default_rng(100 + i).permutation(w.batch * G).astype(np.int32)
+            dc.block_table.copy_(torch.from_numpy(perm.reshape(w.batch, G)))
+        else:
+            dc = hq.DeviceCache(cfg, device=dev)
         dc.set_basis(U)
         dc.append(K, V, 0)
         caches.append(dc)
@@ -269,12 +277,13 @@ def main():
         "workload": f"{w.name}: {desc}, Hq {w.n_q_heads}, Hkv {w.n_kv_heads}, d {w.head_dim}, batch {w.batch}, "
                     f"context {n_ctx}, 2-bit keys + rank-{w.rank} 4-bit side code"
                     + ("" if append_only else f", {w.value_mode} {kinds[w.value_dtype]} values")
-                    + (f", {n_layers} layers" if n_layers > 1 else ""),
+                    + (f", {n_layers} layers" if n_layers > 1 else "")
+                    + (", paged (shuffled 32-token pages)" if args.paged else ""),
         "batch": w.batch, "n_ctx": n_ctx, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
         "head_dim": w.head_dim, "rank": w.rank, "layers": n_layers,
         "step": ("headq_cache_append of the whole prefill (keys)" if append_only else
                  "per layer: append newest 32-token group + decode over the full context"),
-        "cache_copies": len(caches), "n_splits": args.splits or "auto",
+        "cache_copies": len(caches), "n_splits": args.splits or "auto", "paged": bool(args.paged),
     }
     result = {
         "metric": METRIC,
@@ -314,7 +323,7 @@ def main():
         dec_s = float(decode_ms.mean()) / 1e3
         achieved = alg_bytes / dec_s / 1e9
         mfma = w.value_mode == "q2" or w.value_dtype == "bf16"
-        traffic = traffic_per_launch(w.name)
+        traffic = None if args.paged else traffic_per_launch(w.name)  # counters were taken on contiguous caches
         result.update({
             "value": tok_heads / (ms_per_step / 1e3),
             "unit": "query-head cached tokens/s",

@@ -202,17 +202,18 @@ struct GroupRaw {
 };
 
 template <int D, int R, bool VQ2>
-__device__ __forceinline__ void load_group(GroupRaw<D, R, VQ2>& g, const Stream& s_stream, const DecodeArgs& a, int b,
-                                           int h, int lane, int n, int quad, int gi_in) {
+__device__ __forceinline__ void load_group(GroupRaw<D, R, VQ2>& g, const Stream& s_stream, const DecodeArgs& a, int h,
+                                           int page_v, int lane, int n, int quad, int gi_in) {
   using KS = KSide<D, R, VQ2>;
   // the group index is wave-uniform; saying so keeps every group offset in a scalar register
   // (a per-lane offset would make the compiler loop over the lanes around each buffer load)
   int gi = __builtin_amdgcn_readfirstlane(gi_in);
   Stream s = s_stream;
   if (a.map.block_table) {
-    // paged cache: this group's block in the pools, one buffer resource per array from its own
-    // 64-bit base (pools may exceed the 32-bit offset range of a single resource)
-    int64_t page = __builtin_amdgcn_readfirstlane(a.map.block_table[(int64_t)b * a.map.max_pages + gi]);
+    // paged cache: this group's block in the pools (page_v from request_page), one buffer
+    // resource per array from its own 64-bit base (pools may exceed the 32-bit offset range of a
+    // single resource)
+    int64_t page = __builtin_amdgcn_readfirstlane(page_v);
     page = page < 0 ? 0 : (page >= a.map.n_pages ? a.map.n_pages - 1 : page);
     const int64_t blk = page * a.hkv + h;
     s.kcode = make_rsrc(a.kcode + blk * KS::KC, KS::KC);
@@ -248,6 +249,14 @@ __device__ __forceinline__ void load_group(GroupRaw<D, R, VQ2>& g, const Stream&
       g.v[ct] = __builtin_amdgcn_raw_buffer_load_b128(s.v, ct < 4 ? v0 : v0 + 4096, v_goff + off, kStream);
     }
   }
+}
+
+// Page of group gi in this row's block table (paged caches; 0 otherwise), requested one group pair
+// ahead as a vector load: the wait for it then falls after the group loads issued before it (the
+// vector memory counter is in order) instead of stalling the next group's requests.
+__device__ __forceinline__ int request_page(const DecodeArgs& a, __amdgpu_buffer_rsrc_t table_row, int gi) {
+  const int off = __builtin_amdgcn_readfirstlane(gi * 4);  // wave-uniform: no loop over the lanes
+  return a.map.block_table ? (int)__builtin_amdgcn_raw_buffer_load_b32(table_row, 0, off, 0) : 0;
 }
 
 // Per-lane operands fixed for the whole kernel.
@@ -623,13 +632,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int rot = n_groups > 0 ? (int)((bh * 40503) % n_groups) : 0;
   auto group_at = [&](int j) { const int x = j + rot; return x >= n_groups ? x - n_groups : x; };
   const int j_begin = split * kWaves + wave;
+  const __amdgpu_buffer_rsrc_t table_row =
+      make_rsrc(a.map.block_table ? a.map.block_table + (int64_t)b * a.map.max_pages : nullptr,
+                a.map.block_table ? a.map.max_pages * 4 : 0);
+  auto page_at = [&](int j) { return j < n_groups ? request_page(a, table_row, group_at(j)) : 0; };
+  int pa = 0, pb = 0;          // pages of the next groups loaded into ga / gb (paged caches)
   GroupRaw<D, R, VQ2> ga, gb;  // ping-pong register sets: one group computed while the next loads
+  auto first_loads = [&]() {
+    if (j_begin < n_groups) load_group<D, R, VQ2>(ga, s, a, h, page_at(j_begin), lane, n, quad, group_at(j_begin));
+    if (j_begin + W < n_groups)
+      load_group<D, R, VQ2>(gb, s, a, h, page_at(j_begin + W), lane, n, quad, group_at(j_begin + W));
+    pa = page_at(j_begin + 2 * W);
+    pb = page_at(j_begin + 3 * W);
+  };
   // the wave that takes the unfinished group requests its first groups after it (fewer live registers)
   const bool tail_wave = n_ctx % kGroup && split == 0 && wave == 0;
-  if (!tail_wave) {
-    if (j_begin < n_groups) load_group<D, R, VQ2>(ga, s, a, b, h, lane, n, quad, group_at(j_begin));
-    if (j_begin + W < n_groups) load_group<D, R, VQ2>(gb, s, a, b, h, lane, n, quad, group_at(j_begin + W));
-  }
+  if (!tail_wave) first_loads();
   __syncthreads();
 
   // ---- prologue (whole workgroup): per-head power-of-two query scale, U^T q
@@ -696,8 +714,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // ---- the unfinished last group (exact, from the tails), by one wave per stream
   if (tail_wave) {
     process_tail<D>(a, n_ctx, bh, b, hq0, g, n, quad, qs, f.inv_scale, o_acc, z_acc, VQ2 ? NG : 0, m_run, l_run);
-    if (j_begin < n_groups) load_group<D, R, VQ2>(ga, s, a, b, h, lane, n, quad, group_at(j_begin));
-    if (j_begin + W < n_groups) load_group<D, R, VQ2>(gb, s, a, b, h, lane, n, quad, group_at(j_begin + W));
+    first_loads();
   }
 
   // ---- this wave's groups
@@ -705,10 +722,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   for (int j = j_begin; j < n_groups; j += 2 * W) {
     process_group<D, R, VQ2>(ga, f, slot, a, group_at(j), b, hq0, g, lane, n, quad, o_acc, z_acc, m_run, l_run);
     if (j + W >= n_groups) break;
-    if (j + 2 * W < n_groups) load_group<D, R, VQ2>(ga, s, a, b, h, lane, n, quad, group_at(j + 2 * W));
+    if (j + 2 * W < n_groups) {
+      load_group<D, R, VQ2>(ga, s, a, h, pa, lane, n, quad, group_at(j + 2 * W));
+      pa = page_at(j + 4 * W);
+    }
     process_group<D, R, VQ2>(gb, f, slot, a, group_at(j + W), b, hq0, g, lane, n, quad, o_acc, z_acc, m_run,
                              l_run);
-    if (j + 3 * W < n_groups) load_group<D, R, VQ2>(gb, s, a, b, h, lane, n, quad, group_at(j + 3 * W));
+    if (j + 3 * W < n_groups) {
+      load_group<D, R, VQ2>(gb, s, a, h, pb, lane, n, quad, group_at(j + 3 * W));
+      pb = page_at(j + 5 * W);
+    }
   }
   if constexpr (VQ2) {
     // zero part of the 2-bit values: sum over the four token quads, added to every channel of
