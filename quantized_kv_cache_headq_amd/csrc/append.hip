@@ -4,19 +4,22 @@
 // each key (k_base = B_b(k)), form the residual e = k - k_base, project it on the calibration
 // basis and side-quantize the projection, z = Q_q(U_h^T e); the cache keeps the base code and z.
 //
-// One launch writes keys and values. A workgroup (256 threads, 4 wave64) owns two 32-token
-// groups of one (b, h) stream (the second one duplicated, with its stores masked, when the
-// token range holds an odd number of groups):
-//   1. both 32 x d key tiles are loaded with 128-bit loads into LDS as f32
+// One launch writes keys and values. A workgroup (256 threads, 4 wave64) owns GPW 32-token
+// groups of one (b, h) stream: two for long writes (the second one duplicated, with its stores
+// masked, when the token range holds an odd number of groups), one for small launches such as
+// the one-group append of a decode step, where the workgroup's latency is the whole cost:
+//   1. the 32 x d key tiles are loaded with 128-bit loads into LDS as f32
 //   2. per (group, channel): min/max over the 32 tokens -> binary16 step s and zero z (kmeta)
 //   3. per (token, 16 channels): 2-bit codes (one 32-bit store) and residuals (back into LDS)
-//   4. projection y = U^T e: wave w owns a run of components and lane l owns token row l of the
-//      64, so U_h is wave-uniform and comes through scalar loads while the residual streams
-//      from LDS; every component is one sequential f32 fma chain over channels 0..d-1 (the
-//      canonical order that makes the side codes reproducible). The per-token maximum |y| is
-//      combined across the waves in LDS; each wave then side-quantizes and packs its components.
-//   5. values (when given): dense values are transposed into the channel-major group layout,
-//      2-bit values quantized per (token, 32-channel group) into the matrix-operand layout.
+//   4. projection y = U^T e: a slot (a wave for two groups, a half-wave for one) owns a run of
+//      components and its lane owns one token row, so U_h is uniform over the slot (scalar loads
+//      for long writes, LDS broadcast for small ones) while the residual streams from LDS; every
+//      component is one sequential f32 fma chain over channels 0..d-1 (the canonical order that
+//      makes the side codes reproducible). The per-token maximum |y| is combined across the
+//      slots in LDS; each slot then side-quantizes and packs its components.
+//   5. values (when given): dense values are transposed into the channel-major group layout
+//      (8 tokens of a channel per 16-byte store), 2-bit values quantized per (token, 32-channel
+//      group) into the matrix-operand layout.
 //
 // Numerics: no contraction anywhere in this file (every fma is explicit), IEEE division,
 // rint = round half to even, binary16 conversion with round to nearest even.
@@ -30,8 +33,6 @@ namespace headq {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kGpw = 2;               // 32-token groups per workgroup
-constexpr int kRows = kGpw * kGroup;  // token rows per workgroup (one per lane of a wave)
 
 typedef const __attribute__((address_space(4))) float* const_f32_ptr;  // read through scalar loads
 
@@ -59,8 +60,8 @@ __device__ __forceinline__ uint32_t base_code(float k, float z, float inv) {
   return (uint32_t)c;
 }
 
-// The workgroup's two groups: row = 32 * gl + t. The appended range [start, end) touches groups
-// floor(start/32) .. ceil(end/32)-1; group gl of this workgroup is touched group 2*blockIdx.x + gl,
+// The workgroup's GPW groups: row = 32 * gl + t. The appended range [start, end) touches groups
+// floor(start/32) .. ceil(end/32)-1; group gl of this workgroup is touched group GPW*blockIdx.x + gl,
 // clamped to the last one (a duplicate whose stores are masked) when the count is odd. A group is
 // encoded only if it is whole once the range is in (32 * (g + 1) <= end); the rows of a group
 // before `start` come from the dense tail, rows at or past `end` do not exist yet. (Plain scalars
@@ -73,13 +74,14 @@ struct Tile {
   __device__ bool whole(int gl) const { return gl ? w1 : w0; }
 };
 
+template <int GPW>
 __device__ __forceinline__ Tile tile_of(const AppendArgs& a, int64_t start) {
   Tile tl;
   tl.bh = (int64_t)blockIdx.z * a.hkv + blockIdx.y;
   const int64_t end = start + a.n_new;
   const int64_t g_first = start / kGroup, n_touch = (end + kGroup - 1) / kGroup - g_first;
-  tl.g0 = g_first + (int64_t)blockIdx.x * kGpw;
-  const bool real1 = (int64_t)blockIdx.x * kGpw + 1 < n_touch;
+  tl.g0 = g_first + (int64_t)blockIdx.x * GPW;
+  const bool real1 = GPW > 1 && (int64_t)blockIdx.x * GPW + 1 < n_touch;
   tl.g1 = real1 ? tl.g0 + 1 : tl.g0;
   tl.w0 = (tl.g0 + 1) * kGroup <= end;
   tl.w1 = real1 && (tl.g1 + 1) * kGroup <= end;
@@ -101,11 +103,12 @@ __device__ __forceinline__ const void* row_src(const AppendArgs& a, int64_t star
   return nullptr;
 }
 
-// Load the 64 rows of f32/bf16 input (element stride 1 along channels, token stride ts) into an
-// f32 LDS tile with row pitch P, with 128-bit loads; rows that do not exist yet read as zero.
-template <int D, int P, bool BF16>
+// Load the 32 * GPW rows of f32/bf16 input (element stride 1 along channels, token stride ts)
+// into an f32 LDS tile with row pitch P, with 128-bit loads; rows that do not exist yet read as zero.
+template <int D, int P, bool BF16, int GPW>
 __device__ __forceinline__ void load_rows(float (*dst)[P], const AppendArgs& a, int64_t start, const void* base,
                                           int64_t ts, const void* tail, const Tile& tl) {
+  constexpr int kRows = GPW * kGroup;
   constexpr int kElem = BF16 ? 8 : 4;  // elements per 16-byte load
   constexpr int kChunks = D / kElem;   // 16-byte chunks per row
   for (int i = threadIdx.x; i < kRows * kChunks; i += kThreads) {
@@ -154,23 +157,26 @@ __device__ __forceinline__ void write_tails(const AppendArgs& a, int64_t start, 
 // UL: U_h staged in LDS and read with wave-uniform (broadcast) addresses, the shorter critical
 // path for small launches (one group per stream, as in a decode step); otherwise U_h comes
 // through scalar loads, which leaves more LDS for concurrent workgroups of a long prefill.
-template <int D, int R, bool KBF16, bool UL>
+template <int D, int R, bool KBF16, bool UL, int GPW>
 __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
+  static_assert(GPW == 2 || (GPW == 1 && UL), "a half-wave projection slot reads U_h from LDS");
+  constexpr int kRows = GPW * kGroup;      // token rows per workgroup (one per lane of a slot)
   constexpr int P = D + 1;  // LDS row pitch (floats): a column read by 64 rows spreads over the banks
-  // components per wave: r/4, at least 2 so that every wave packs whole bytes (r = 4 uses two waves)
-  constexpr int CW = R / 4 >= 2 ? R / 4 : 2;
-  constexpr int NWP = R > 0 ? R / CW : 0;  // waves that project
+  constexpr int SLOTS = GPW == 2 ? 4 : 8;  // projection slots: waves (64 rows) or half-waves (32 rows)
+  // components per slot: r/SLOTS, at least 2 so that every slot packs whole bytes
+  constexpr int CW = R / SLOTS >= 2 ? R / SLOTS : 2;
+  constexpr int NWP = R > 0 ? R / CW : 0;  // slots that project
   constexpr int NG = D / 32;               // 32-channel groups (2-bit values)
   __shared__ float ke[kRows][P];           // keys, then residuals; values in step 5
-  __shared__ float s_s[kGpw * D], z_s[kGpw * D], inv_s[kGpw * D];
-  __shared__ float amax_s[4][kRows];
+  __shared__ float s_s[GPW * D], z_s[GPW * D], inv_s[GPW * D];
+  __shared__ float amax_s[SLOTS][kRows];
   __shared__ float U_s[UL && R > 0 ? D * R : 1];
 
   const int h = blockIdx.y, b = blockIdx.z;
   // this row's append position; a row that would pass the capacity is left untouched
   const int64_t st = a.row_start ? (int64_t)a.row_start[b] : a.start;
   if (st < 0 || st + a.n_new > a.cap) return;
-  const Tile tl = tile_of(a, st);
+  const Tile tl = tile_of<GPW>(a, st);
   const int tid = threadIdx.x, lane = tid % 64;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
   const char* kin = (const char*)a.k + ((int64_t)b * a.ks_b + (int64_t)h * a.ks_h) * (KBF16 ? 2 : 4);
@@ -199,7 +205,7 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
     }
   }
 
-  load_rows<D, P, KBF16>(ke, a, st, kin, a.ks_t, a.ktail, tl);
+  load_rows<D, P, KBF16, GPW>(ke, a, st, kin, a.ks_t, a.ktail, tl);
   if constexpr (UL && R > 0) {
     const float4* Ug = reinterpret_cast<const float4*>(a.U + (int64_t)h * D * R);
     for (int i = tid; i < D * R / 4; i += kThreads) reinterpret_cast<float4*>(U_s)[i] = Ug[i];
@@ -207,9 +213,10 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
   __syncthreads();
 
   // 2. per (group, channel) step and zero (binary16) over the 32 tokens
-  for (int i = tid; i < kGpw * D; i += kThreads) {
+  for (int i = tid; i < GPW * D; i += kThreads) {
     const int gl = i / D, c = i % D;
     float lo = ke[gl * kGroup][c], hi = lo;
+#pragma unroll
     for (int t = 1; t < kGroup; ++t) {
       const float x = ke[gl * kGroup + t][c];
       lo = x < lo ? x : lo;
@@ -249,14 +256,15 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
 
   if constexpr (R > 0) {
     __syncthreads();
-    // 4. side code. Wave w < NWP projects components [w*CW, (w+1)*CW) of token row `lane`.
-    const int row = lane, gl = row / kGroup;
+    // 4. side code. Slot w < NWP projects components [w*CW, (w+1)*CW) of its lane's token row.
+    const int row = lane % kRows, gl = row / kGroup;
+    const int slot = GPW == 2 ? wave : 2 * wave + lane / kGroup;
     float y[CW];
 #pragma unroll
     for (int j = 0; j < CW; ++j) y[j] = 0.0f;
-    if (wave < NWP) {
+    if (slot < NWP) {
       if constexpr (UL) {
-        const float* Uw = U_s + wave * CW;
+        const float* Uw = U_s + slot * CW;
 #pragma unroll 8
         for (int c = 0; c < D; ++c) {
           const float e = ke[row][c];
@@ -279,9 +287,9 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
       const float m = __builtin_fabsf(y[j]);
       amax = m > amax ? m : amax;
     }
-    amax_s[wave][row] = amax;
+    amax_s[slot][row] = amax;
     __syncthreads();
-    if (wave < NWP) {
+    if (slot < NWP) {
 #pragma unroll
       for (int w = 0; w < NWP; ++w) {
         const float m = amax_s[w][row];
@@ -301,14 +309,14 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
       if (tl.whole(gl)) {
         const int64_t tok = row_token(tl, row);
         const int64_t trow = a.map.row(b, h, tok);
-        uint8_t* dst = a.scode + trow * (R / 2) + wave * (CW / 2);
+        uint8_t* dst = a.scode + trow * (R / 2) + slot * (CW / 2);
         if constexpr (CW == 8)
           *reinterpret_cast<uint32_t*>(dst) = packed;
         else if constexpr (CW == 4)
           *reinterpret_cast<uint16_t*>(dst) = (uint16_t)packed;
         else
           *dst = (uint8_t)packed;
-        if (wave == 0) a.ssc[trow] = sg_bits;
+        if (slot == 0) a.ssc[trow] = sg_bits;
       }
     }
   }
@@ -336,15 +344,23 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
       }
     }
     __syncthreads();
-    for (int i = tid; i < kRows * D; i += kThreads) {
-      const int gl = i / (D * kGroup), c = (i / kGroup) % D, t = i % kGroup;
+    // 8 tokens of one channel per thread: one 16-byte store (bf16) or two (f32)
+    for (int i = tid; i < kRows * D / 8; i += kThreads) {
+      const int t8 = i % 4, c = (i / 4) % D, gl = i / (4 * D);
       if (!tl.whole(gl)) continue;
-      const int64_t idx = (a.map.block(b, h, tl.group(gl)) * D + c) * kGroup + t;
-      const uint32_t x = raw[gl * kGroup + t][c];
-      if (vbf)
-        ((uint16_t*)a.vdense)[idx] = (uint16_t)x;
-      else
-        ((uint32_t*)a.vdense)[idx] = x;
+      const int row0 = gl * kGroup + t8 * 8;
+      const int64_t idx = (a.map.block(b, h, tl.group(gl)) * D + c) * kGroup + t8 * 8;
+      uint32_t x[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) x[k] = raw[row0 + k][c];
+      if (vbf) {
+        *reinterpret_cast<uint4*>((uint16_t*)a.vdense + idx) =
+            make_uint4(x[0] | x[1] << 16, x[2] | x[3] << 16, x[4] | x[5] << 16, x[6] | x[7] << 16);
+      } else {
+        uint4* dst = reinterpret_cast<uint4*>((uint32_t*)a.vdense + idx);
+        dst[0] = make_uint4(x[0], x[1], x[2], x[3]);
+        dst[1] = make_uint4(x[4], x[5], x[6], x[7]);
+      }
     }
   } else {
     // 2-bit values: per (token, 32-channel group) min/max grid, codes in matrix-operand order
@@ -366,10 +382,11 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
       }
     }
     __syncthreads();
-    // grid of (row, channel group) in the key step/zero arrays, now free: kRows * NG = kGpw * D
+    // grid of (row, channel group) in the key step/zero arrays, now free: kRows * NG = GPW * D
     for (int i = tid; i < kRows * NG; i += kThreads) {
       const int row = i % kRows, gc = i / kRows, gl = row / kGroup, t = row % kGroup;
       float lo = ke[row][gc * 32], hi = lo;
+#pragma unroll
       for (int c = 1; c < 32; ++c) {
         const float x = ke[row][gc * 32 + c];
         lo = x < lo ? x : lo;
@@ -391,7 +408,7 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
     // group block of d*8 code bytes: lane l = 16*quad + n owns d/8 bytes, two per 16-channel
     // tile ct (channel 16*ct + n, tokens 8*quad .. 8*quad+7); token item i = 4q + 2b + e of the
     // eight sits in byte b of the pair at bit 4e + 2q
-    for (int i = tid; i < kGpw * D * 8; i += kThreads) {
+    for (int i = tid; i < GPW * D * 8; i += kThreads) {
       const int gl = i / (D * 8), byte = i % (D * 8);
       const int ln = byte / (D / 8), within = byte % (D / 8);
       const int c = 16 * (within / 2) + ln % 16, bb = within % 2, gc = c / 32;
@@ -420,18 +437,20 @@ hipError_t launch_dr(const AppendArgs& a, hipStream_t s) {
   const int64_t end = a.start + a.n_new;
   // groups the range touches; with per-row positions, the most any row can touch
   const int64_t n_touch = a.row_start ? (a.n_new + kGroup - 1) / kGroup + 1 : (end + kGroup - 1) / kGroup - a.start / kGroup;
-  dim3 grid((unsigned)((n_touch + kGpw - 1) / kGpw), (unsigned)a.hkv, (unsigned)a.batch);
-  const bool small = (int64_t)grid.x * grid.y * grid.z <= 1024;  // at most ~4 workgroups per CU
+  // small launches (at most ~8 groups per CU): one group per workgroup, U_h from LDS; long
+  // writes: two groups per workgroup, U_h through scalar loads
+  const bool small = n_touch * a.hkv * a.batch <= 2048;
+  dim3 grid((unsigned)(small ? n_touch : (n_touch + 1) / 2), (unsigned)a.hkv, (unsigned)a.batch);
   if (a.key_bf16) {
     if (small)
-      hipLaunchKernelGGL((append_kernel<D, R, true, true>), grid, dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((append_kernel<D, R, true, true, 1>), grid, dim3(kThreads), 0, s, a);
     else
-      hipLaunchKernelGGL((append_kernel<D, R, true, false>), grid, dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((append_kernel<D, R, true, false, 2>), grid, dim3(kThreads), 0, s, a);
   } else {
     if (small)
-      hipLaunchKernelGGL((append_kernel<D, R, false, true>), grid, dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((append_kernel<D, R, false, true, 1>), grid, dim3(kThreads), 0, s, a);
     else
-      hipLaunchKernelGGL((append_kernel<D, R, false, false>), grid, dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((append_kernel<D, R, false, false, 2>), grid, dim3(kThreads), 0, s, a);
   }
   return hipGetLastError();
 }

@@ -17,10 +17,10 @@ pytestmark = pytest.mark.gpu
 
 
 def _sampled(wname, streams, out_bf16=False, batch=None, n_splits=0):
-    w = synth.WORKLOADS[wname]
+    w = synth.WORKLOADS[wname] if isinstance(wname, str) else wname
     if batch is not None:
         w = synth.scaled(w, batch=batch)
-    say("fullsize", wname, f"B={w.batch} T={w.n_ctx} streams={streams} splits={n_splits or 'auto'}")
+    say("fullsize", w.name, f"B={w.batch} T={w.n_ctx} streams={streams} splits={n_splits or 'auto'}")
     U = orc.calibrate(synth.calibration_queries(w), w.n_kv_heads, w.rank)[0]
     dc, K, V = gpu_cache(w, U)
     q = synth.decode_queries(w)
@@ -68,3 +68,10 @@ def test_qwen14b_fullkv_full_context_sampled():
     workgroup of four waves per stream: 64 x 8 streams give one split each); the batch is cut to
     4 rows, which leaves every stream's work unchanged."""
     _sampled("qwen14b_fullkv", [(0, 0), (3, 7), (2, 5)], out_bf16=True, batch=4, n_splits=1)
+
+
+def test_long_f32_write_two_groups_per_workgroup():
+    """A write of more than 2048 groups takes the long-write append (two groups per workgroup,
+    U_h through scalar loads); f32 keys and values, so also the vector decode kernel."""
+    w = synth.scaled(synth.WORKLOADS["tiny"], n_q_heads=8, n_kv_heads=4, batch=8, n_ctx=4096)
+    _sampled(w, [(0, 0), (7, 3), (4, 1)])
