@@ -9,6 +9,9 @@ Sources ("Technische Samenvatting: HeadQ ...", the Dutch technical summary):
         weighs each token's value distortion by p_j^2.
   §4    controls: null-space intervention with a non-equivariant fixed-grid quantizer,
         same-budget counterexamples, query-PCA versus random bases, wrong-sign correction.
+
+score_diagnostics() applies these definitions to a packed cache: the cache's corrected logits
+(the oracle decode) against the exact scores of reference keys, per (batch row, query head).
 """
 from __future__ import annotations
 
@@ -59,6 +62,46 @@ def a2_surrogate(p: np.ndarray, dV: np.ndarray) -> float:
     p = np.asarray(p, np.float64)
     dV = np.asarray(dV, np.float64)
     return float(np.sum(p * p * np.sum(dV * dV, axis=-1)))
+
+
+STATS = ("fisher_var", "kl", "mean_ds", "max_abs_ds", "a2", "entropy")
+
+
+def score_diagnostics(cache, q, U, n_ctx, kappa, K_ref, V_ref=None, value_mode=0, value_dtype=1):
+    """Score-space diagnostics of a packed cache against the keys (and values) it was written
+    from, for every (b, query head), over the first n_ctx tokens. Returns f64 [B][Hq][6] in the
+    order of STATS:
+      fisher_var  Var_p(ds) with p = softmax(s), s_j = q.k_j/sqrt(d) from the reference keys and
+                  ds_j = s_hat_j - s_j, s_hat the cache's corrected logits (kappa scales the
+                  correction) — the Fisher-weighted score error of §2.1
+      kl          KL(p || softmax(s_hat)), by its definition
+      mean_ds     E_p[ds] (the softmax-null part of the error)
+      max_abs_ds  max_j |ds_j|
+      a2          sum_j p_j^2 |v_hat_j - v_j|^2, the A^2 surrogate of §2.2 (NaN without V_ref)
+      entropy     -sum_j p_j log p_j of the exact attention
+    q: f32 [B][Hq][d]; K_ref, V_ref: f32 [B][Hkv][>= n_ctx][d] (exact widenings of the stored
+    dtypes). Query head a reads KV head a // (Hq / Hkv)."""
+    from . import oracle as orc
+    s_hat, _ = orc.decode(cache, q, U, n_ctx, kappa, value_mode, value_dtype)
+    B, Hq, d = q.shape
+    Hkv = K_ref.shape[1]
+    g = Hq // Hkv
+    out = np.zeros((B, Hq, len(STATS)), np.float64)
+    for b in range(B):
+        for h in range(Hkv):
+            K = np.asarray(K_ref[b, h, :n_ctx], np.float64)
+            dV = None
+            if V_ref is not None:
+                dV = orc.value_rows(cache, b, h, n_ctx, value_mode, value_dtype) - np.asarray(V_ref[b, h, :n_ctx],
+                                                                                           np.float64)
+            for a in range(h * g, (h + 1) * g):
+                s = scores(q[b, a], K)
+                ds = s_hat[b, a] - s
+                p = softmax(s)
+                out[b, a] = (fisher_variance(p, ds), kl(p, softmax(s_hat[b, a])), float(p @ ds),
+                             float(np.max(np.abs(ds))), np.nan if dV is None else a2_surrogate(p, dV),
+                             float(-np.sum(p[p > 0] * np.log(p[p > 0]))))
+    return out
 
 
 def fixed_grid_quantize(K: np.ndarray, step: float, levels: int) -> np.ndarray:

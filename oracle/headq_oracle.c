@@ -504,3 +504,28 @@ int orc_decode(int d, int hq, int hkv, int r, int value_mode, int value_dtype, i
   free(qd); free(qu); free(s); free(o);
   return 0;
 }
+
+/* ------------------------------------------------------------------------------------------ */
+/* Value rows of one (b, h) stream as the cache holds them, in fp64 ([TS] §2.2: the operands v_j
+ * of the readout): dense values as stored, 2-bit values unpacked as code * s + z, and the tokens
+ * past the last whole group from the dense tail. out: f64 [n_ctx][d]. */
+int orc_value_rows(int d, int value_mode, int value_dtype, int hkv, int64_t cap, int64_t n_ctx,
+                   const void* vdense, const uint8_t* vcode, const uint16_t* vmeta, const void* vtail, int b,
+                   int h, double* out) {
+  if (d <= 0 || cap % GROUP || n_ctx < 0 || n_ctx > cap || b < 0 || h < 0 || h >= hkv || !out) return -1;
+  const int64_t n_full = n_ctx / GROUP * GROUP;
+  if (n_full < n_ctx && !vtail) return -1;
+  if (value_mode == 0 && !vdense) return -1;
+  if (value_mode == 1 && (!vcode || !vmeta || d % GROUP)) return -1;
+  const int64_t bh = (int64_t)b * hkv + h;
+  const int vb = (value_dtype == 0) ? 4 : 2;
+  const void* vd = vdense ? (const void*)((const uint8_t*)vdense + bh * cap * d * vb) : NULL;
+  const uint8_t* vc = vcode ? vcode + bh * (cap / GROUP) * d * 8 : NULL;
+  const uint16_t* vm = vmeta ? vmeta + bh * (cap / GROUP) * 2 * d : NULL;
+  for (int64_t j = 0; j < n_ctx; ++j)
+    for (int c = 0; c < d; ++c)
+      out[j * d + c] = j >= n_full ? tail_at(vtail, value_dtype, (bh * GROUP + j % GROUP) * d + c)
+                                   : v_hat(value_mode, value_dtype, vd, vc, vm, d, j, c);
+  return 0;
+}
+

@@ -92,6 +92,13 @@ int orc_decode(int d, int hq, int hkv, int r, int value_mode, int value_dtype, i
                int key_dtype, const void* ktail, const void* vtail, const float* U, const float* q, double kappa,
                int b_begin, int b_end, double* logits, double* out);
 
+/* Value rows of stream (b, h) as the cache holds them, in fp64: out [n_ctx][d] (dense values as
+ * stored, 2-bit values as code * s + z, tokens past the last whole group from vtail). Cache
+ * buffers as for orc_decode. */
+int orc_value_rows(int d, int value_mode, int value_dtype, int hkv, int64_t cap, int64_t n_ctx,
+                   const void* vdense, const uint8_t* vcode, const uint16_t* vmeta, const void* vtail, int b,
+                   int h, double* out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -59,6 +59,7 @@ def lib():
         L.orc_pack_vcode.argtypes = [I, I64, P, P]
         L.orc_pack_vmeta.argtypes = [I, I64, P, P, P]
         L.orc_decode.argtypes = [I, I, I, I, I, I, I, I64, I64, P, P, P, P, P, P, P, I, P, P, P, P, D, I, I, P, P]
+        L.orc_value_rows.argtypes = [I, I, I, I, I64, I64, P, P, P, P, I, I, P]
         _lib = L
     return _lib
 
@@ -286,3 +287,16 @@ def decode(cache, q, U, n_ctx, kappa=1.0, value_mode=0, value_dtype=1, b_range=N
                             _p(arrs.get("vtail")), _p(Uc), _p(q), float(kappa), b0, b1, _p(logits), _p(out)),
            "decode")
     return logits, out
+
+
+def value_rows(cache, b, h, n_ctx, value_mode=0, value_dtype=1):
+    """Value rows of stream (b, h) as the cache holds them: f64 [n_ctx][d] (dense as stored,
+    2-bit as code * s + z, the unfinished group from the tail)."""
+    arrs = {k: np.ascontiguousarray(val) for k, val in cache.items()}
+    B, Hkv, cap, _ = arrs["kcode"].shape
+    d = arrs["kmeta"].shape[-1]
+    out = np.zeros((n_ctx, d), np.float64)
+    _check(lib().orc_value_rows(d, value_mode, value_dtype, Hkv, cap, n_ctx, _p(arrs.get("v")), _p(arrs.get("vcode")),
+                                _p(arrs.get("vmeta")), _p(arrs.get("vtail")), b, h, _p(out)), "value_rows")
+    return out
+
