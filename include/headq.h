@@ -201,6 +201,43 @@ headq_status headq_decode_attn(const headq_config* cfg, const headq_cache* cache
                                float* logits_dbg,
                                int32_t n_splits, void* ws, size_t* ws_bytes, void* stream);
 
+/* Statistics of headq_score_diagnostics, per (batch row, query head). */
+enum {
+  HEADQ_DIAG_FISHER_VAR = 0, /* Var_p(ds): Fisher-weighted variance of the score error */
+  HEADQ_DIAG_KL = 1,         /* KL(p || p_hat) of the exact against the cache's attention */
+  HEADQ_DIAG_MEAN_DS = 2,    /* E_p[ds]: the softmax-null part of the score error */
+  HEADQ_DIAG_MAX_ABS_DS = 3, /* max_j |ds_j| */
+  HEADQ_DIAG_A2 = 4,         /* sum_j p_j^2 |v_hat_j - v_j|^2 (NaN without reference values) */
+  HEADQ_DIAG_ENTROPY = 5,    /* -sum_j p_j log p_j of the exact attention */
+  HEADQ_DIAG_NSTAT = 6
+};
+
+/*
+ * headq_score_diagnostics — score-space diagnostics of the cache against the keys (and values)
+ * it was written from, for calibration sweeps and the method's controls (wrong sign through
+ * corr_scale = -1, random or other bases through U, rank 0). Summary §2.1: a key error reaches
+ * the model only through the score error ds_j = s_hat_j - s_j, and the local KL between exact and
+ * perturbed attention is its Fisher-weighted variance; §2.2: the A^2 surrogate weighs each
+ * token's value distortion by p_j^2. Here s_j = q.k_j/sqrt(d) from the reference keys,
+ * p = softmax(s), s_hat_j the cache's corrected logit of §3 step 3 (base key plus corr_scale
+ * times the side correction; tokens in the tails are exact), v_hat_j the cache's value. All
+ * arithmetic is f64; KL is evaluated as log E_p[exp(ds)] - E_p[ds].
+ *   q        device [B][Hq][d] in query_dtype (contiguous)
+ *   k_ref    device reference keys in key_dtype, element (b, h, t, c) at
+ *            k_ref[b*ks[0] + h*ks[1] + t*ks[2] + c] (as for headq_cache_append)
+ *   v_ref    device reference values in value_dtype, or NULL (HEADQ_DIAG_A2 is then NaN)
+ *   n_ctx    tokens, 1 <= n_ctx <= capacity (n_ctx % 32 != 0 needs both tails)
+ *   stats    device f64 [B][Hq][HEADQ_DIAG_NSTAT] (written)
+ *   n_splits workgroups per (b, h); 0 = automatic, else 1..ceil(n_ctx / 64)
+ *   ws, ws_bytes  device workspace, 16-byte aligned; with ws == NULL only *ws_bytes is set
+ *            (nothing launched). No zero-fill needed. Calls sharing ws must not overlap.
+ * Errors: NULL, SHAPE, ALIGN, CAPACITY, WORKSPACE, UNSUPPORTED, HIP.
+ */
+headq_status headq_score_diagnostics(const headq_config* cfg, const headq_cache* cache, const void* q,
+                                     const void* k_ref, const int64_t k_strides[3], const void* v_ref,
+                                     const int64_t v_strides[3], int64_t n_ctx, float corr_scale, double* stats,
+                                     int32_t n_splits, void* ws, size_t* ws_bytes, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* headq_status_string(headq_status s);
 

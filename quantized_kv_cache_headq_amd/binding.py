@@ -23,7 +23,9 @@ STATUS = {
     0: "HEADQ_OK", 1: "HEADQ_ERR_NULL", 2: "HEADQ_ERR_SHAPE", 3: "HEADQ_ERR_ALIGN", 4: "HEADQ_ERR_CAPACITY",
     5: "HEADQ_ERR_WORKSPACE", 6: "HEADQ_ERR_NUMERIC", 7: "HEADQ_ERR_UNSUPPORTED", 8: "HEADQ_ERR_HIP",
 }
-EXPORTS = ("headq_calibrate", "headq_cache_append", "headq_decode_attn", "headq_status_string")
+EXPORTS = ("headq_calibrate", "headq_cache_append", "headq_decode_attn", "headq_score_diagnostics",
+           "headq_status_string")
+DIAG_STATS = ("fisher_var", "kl", "mean_ds", "max_abs_ds", "a2", "entropy")  # HEADQ_DIAG_* order
 
 
 class HeadQError(RuntimeError):
@@ -65,9 +67,10 @@ def load() -> ctypes.CDLL:
         L.headq_calibrate.argtypes = [P, P, I64, P, P]
         L.headq_cache_append.argtypes = [P, P, P, P, P, P, I64, I64, P, P]
         L.headq_decode_attn.argtypes = [P, P, P, I64, P, P, I32, F, P, I32, P, P, P]
+        L.headq_score_diagnostics.argtypes = [P, P, P, P, P, P, P, I64, F, P, I32, P, P, P]
         L.headq_status_string.argtypes = [ctypes.c_int]
         L.headq_status_string.restype = ctypes.c_char_p
-        for fn in ("headq_calibrate", "headq_cache_append", "headq_decode_attn"):
+        for fn in ("headq_calibrate", "headq_cache_append", "headq_decode_attn", "headq_score_diagnostics"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -175,6 +178,29 @@ def headq_decode_attn(cfg: Config, cache: headq_cache, q, n_ctx: int, out, out_d
                                     _stream(stream)), "headq_decode_attn")
 
 
+def diagnostics_workspace_bytes(cfg: Config, n_ctx: int, n_splits: int = 0) -> int:
+    c = cfg.c()
+    nbytes = ctypes.c_size_t(0)
+    _check(load().headq_score_diagnostics(ctypes.byref(c), None, None, None, None, None, None, n_ctx, 1.0, None,
+                                          n_splits, None, ctypes.byref(nbytes), None),
+           "headq_score_diagnostics(size query)")
+    return nbytes.value
+
+
+def headq_score_diagnostics(cfg: Config, cache: headq_cache, q, k_ref, v_ref, n_ctx: int, stats,
+                            corr_scale: float = 1.0, n_splits: int = 0, ws=None, stream=None):
+    """Score-space diagnostics of the cache against reference keys k_ref (and values v_ref, or
+    None) [B][Hkv][>= n_ctx][d] (torch device tensors): stats, a device f64 [B][Hq][6] tensor, gets
+    DIAG_STATS per (b, query head). ws: device buffer of diagnostics_workspace_bytes(...) bytes."""
+    c = cfg.c()
+    nbytes = ctypes.c_size_t(ws.numel() * ws.element_size())
+    vs = _strides3(v_ref) if v_ref is not None else None
+    _check(load().headq_score_diagnostics(ctypes.byref(c), ctypes.byref(cache), _ptr(q), _ptr(k_ref),
+                                          _strides3(k_ref), _ptr(v_ref), vs, n_ctx, float(corr_scale), _ptr(stats),
+                                          n_splits, _ptr(ws), ctypes.byref(nbytes), _stream(stream)),
+           "headq_score_diagnostics")
+
+
 # ------------------------------------------------------------------------------------------------
 # device buffers of one layer's cache (torch for memory only)
 
@@ -227,6 +253,18 @@ class DeviceCache:
         headq_decode_attn(self.cfg, self.c(), q, n_ctx, out, out_dtype, corr_scale, logits_dbg, n_splits, ws, stream,
                           row_len)
         return out
+
+    def score_diagnostics(self, q, k_ref, v_ref, n_ctx: int, corr_scale: float = 1.0, n_splits: int = 0, ws=None,
+                          stream=None):
+        """f64 [B][Hq][6] statistics (DIAG_STATS order) of this cache against k_ref / v_ref."""
+        import torch
+        if ws is None:
+            nb = diagnostics_workspace_bytes(self.cfg, n_ctx, n_splits)
+            ws = torch.empty((nb + 7) // 8, dtype=torch.float64, device=q.device)
+        stats = torch.empty((self.cfg.batch, self.cfg.n_q_heads, len(DIAG_STATS)), dtype=torch.float64,
+                            device=q.device)
+        headq_score_diagnostics(self.cfg, self.c(), q, k_ref, v_ref, n_ctx, stats, corr_scale, n_splits, ws, stream)
+        return stats
 
     def nbytes(self) -> int:
         return sum(t.numel() * t.element_size() for t in (self.kcode, self.kmeta, self.scode, self.ssc, self.v,

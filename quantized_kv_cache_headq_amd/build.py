@@ -16,7 +16,7 @@ CSRC = PKG / "csrc"
 OUT = PKG / "libheadq.so"
 BUILD_DIR = PKG / "_build"
 
-SOURCES = ["headq_api.cpp", "calibrate.cpp", "append.hip", "decode.hip", "decode_mfma.hip"]
+SOURCES = ["headq_api.cpp", "calibrate.cpp", "append.hip", "decode.hip", "decode_mfma.hip", "diagnostics.hip"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

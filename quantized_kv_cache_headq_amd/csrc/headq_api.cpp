@@ -261,3 +261,92 @@ extern "C" headq_status headq_decode_attn(const headq_config* cfg, const headq_c
   hipStream_t s = (hipStream_t)stream;
   return finish(headq::launch_decode(a, s), s);
 }
+
+extern "C" headq_status headq_score_diagnostics(const headq_config* cfg, const headq_cache* cache, const void* q,
+                                                const void* k_ref, const int64_t k_strides[3], const void* v_ref,
+                                                const int64_t v_strides[3], int64_t n_ctx, float corr_scale,
+                                                double* stats, int32_t n_splits, void* ws, size_t* ws_bytes,
+                                                void* stream) {
+  headq_status st = check_config(cfg);
+  if (st != HEADQ_OK) return st;
+  if (!ws_bytes) return HEADQ_ERR_NULL;
+  if (n_ctx < 1) return HEADQ_ERR_SHAPE;
+  if (n_ctx > cfg->capacity) return HEADQ_ERR_CAPACITY;
+  const int64_t n_chunks = (n_ctx + 63) / 64;  // 64-token chunks, one wave each at a time
+  if (n_splits < 0 || n_splits > n_chunks) return HEADQ_ERR_SHAPE;
+  // automatic: about two waves per SIMD over the whole launch, at least one chunk per wave
+  int64_t S = n_splits;
+  if (!S) {
+    const int64_t streams = (int64_t)cfg->batch * cfg->n_kv_heads;
+    S = (2048 + 4 * streams - 1) / (4 * streams);
+    if (S * 4 > n_chunks) S = (n_chunks + 3) / 4;
+    if (S < 1) S = 1;
+  }
+  const size_t need = headq::diag_ws_bytes(cfg->batch, cfg->n_q_heads, cfg->n_kv_heads, cfg->head_dim, cfg->rank,
+                                           (int)S, n_ctx);
+  if (!ws) {
+    *ws_bytes = need;
+    return HEADQ_OK;
+  }
+  if (!cache || !q || !k_ref || !k_strides || !stats) return HEADQ_ERR_NULL;
+  if (v_ref && !v_strides) return HEADQ_ERR_NULL;
+  st = check_cache(cfg, cache);
+  if (st != HEADQ_OK) return st;
+  if (n_ctx % headq::kGroup && (!cache->ktail || (v_ref && !cache->vtail))) return HEADQ_ERR_NULL;
+  if (*ws_bytes < need) return HEADQ_ERR_WORKSPACE;
+  const int kes = cfg->key_dtype == HEADQ_F32 ? 4 : 2;
+  const int ves = cfg->value_dtype == HEADQ_F32 ? 4 : 2;
+  if (!aligned16(q) || !aligned16(k_ref) || !aligned16(stats) || !aligned16(ws) || (v_ref && !aligned16(v_ref)))
+    return HEADQ_ERR_ALIGN;
+  for (int i = 0; i < 3; ++i) {
+    if (k_strides[i] < 0 || (v_ref && v_strides[i] < 0)) return HEADQ_ERR_SHAPE;
+    if ((k_strides[i] * kes) % 16 || (v_ref && (v_strides[i] * ves) % 16)) return HEADQ_ERR_ALIGN;
+  }
+  if (k_strides[2] < cfg->head_dim || (v_ref && v_strides[2] < cfg->head_dim)) return HEADQ_ERR_SHAPE;
+
+  headq::DiagArgs a{};
+  a.d = cfg->head_dim;
+  a.r = cfg->rank;
+  a.hq = cfg->n_q_heads;
+  a.hkv = cfg->n_kv_heads;
+  a.batch = cfg->batch;
+  a.gqa = cfg->n_q_heads / cfg->n_kv_heads;
+  a.cap = cfg->capacity;
+  a.n_ctx = n_ctx;
+  a.n_splits = (int)S;
+  a.key_bf16 = cfg->key_dtype == HEADQ_BF16;
+  a.value_bf16 = cfg->value_dtype == HEADQ_BF16;
+  a.value_mode = cfg->value_mode;
+  a.query_bf16 = cfg->query_dtype == HEADQ_BF16;
+  a.kappa = corr_scale;
+  a.q = q;
+  a.k_ref = k_ref;
+  a.ks_b = k_strides[0];
+  a.ks_h = k_strides[1];
+  a.ks_t = k_strides[2];
+  a.v_ref = v_ref;
+  if (v_ref) {
+    a.vs_b = v_strides[0];
+    a.vs_h = v_strides[1];
+    a.vs_t = v_strides[2];
+  }
+  a.kcode = cache->kcode;
+  a.kmeta = cache->kmeta;
+  a.scode = cache->scode;
+  a.ssc = cache->ssc;
+  a.vdense = cache->v;
+  a.vcode = cache->vcode;
+  a.vmeta = cache->vmeta;
+  a.U = cache->U;
+  a.ktail = cache->ktail;
+  a.vtail = cache->vtail;
+  a.map = map_of(cfg, cache);
+  const int g = a.gqa;
+  a.ws_q = (double*)ws;
+  a.ws_qu = a.ws_q + headq::diag_ws_q_doubles(a.batch, a.hkv, g, a.d);
+  a.ws_part = a.ws_qu + headq::diag_ws_qu_doubles(a.batch, a.hkv, g, a.r);
+  a.ws_dv2 = a.ws_part + (size_t)a.batch * a.hq * S * headq::kDiagPart;
+  a.stats = stats;
+  hipStream_t s = (hipStream_t)stream;
+  return finish(headq::launch_diagnostics(a, s), s);
+}

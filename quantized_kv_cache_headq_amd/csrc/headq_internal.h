@@ -105,6 +105,54 @@ struct DecodeArgs {
   void* out;
 };
 
+struct DiagArgs {
+  int d, r, hq, hkv, batch, gqa;
+  int64_t cap, n_ctx;
+  int n_splits;                // workgroups per (b, h); 4 waves each, 64-token chunks per wave
+  int key_bf16, value_bf16, value_mode, query_bf16;
+  double kappa;                // scale of the side correction in s_hat
+  const void* q;
+  const void* k_ref;           // reference keys (key dtype), element strides below
+  int64_t ks_b, ks_h, ks_t;
+  const void* v_ref;           // reference values (value dtype) or null: no A^2
+  int64_t vs_b, vs_h, vs_t;
+  const uint8_t* kcode;
+  const uint16_t* kmeta;
+  const uint8_t* scode;
+  const uint16_t* ssc;
+  const void* vdense;
+  const uint8_t* vcode;
+  const uint16_t* vmeta;
+  const float* U;
+  const void* ktail;
+  const void* vtail;
+  CacheMap map;
+  double* ws_q;                // [B][Hkv][padded g][d]   queries in f64 (zero rows past g)
+  double* ws_qu;               // [B][Hkv][padded g][max(r, 1)]   U_h^T q in f64
+  double* ws_part;             // [B][Hq][S][8]   split partials (max, six sums, max |ds|)
+  double* ws_dv2;              // [B][Hkv][n_ctx]   |v_hat_j - v_j|^2 (with reference values)
+  double* stats;               // [B][Hq][HEADQ_DIAG_NSTAT]
+};
+
+constexpr int kDiagPart = 8;        // doubles per split partial
+constexpr int kDiagHeadBatch = 4;   // query heads per pass of the diagnostics stream kernel
+__host__ __device__ constexpr int diag_padded_heads(int g) {
+  return (g + kDiagHeadBatch - 1) / kDiagHeadBatch * kDiagHeadBatch;
+}
+// Workspace: queries [B][Hkv][padded g][d] and U_h^T q [B][Hkv][padded g][max(r, 1)] (f64), split
+// partials [B][Hq][S][8], per-token value errors [B][Hkv][n_ctx].
+inline size_t diag_ws_q_doubles(int batch, int hkv, int g, int d) {
+  return (size_t)batch * hkv * diag_padded_heads(g) * d;
+}
+inline size_t diag_ws_qu_doubles(int batch, int hkv, int g, int r) {
+  return (size_t)batch * hkv * diag_padded_heads(g) * (r > 0 ? r : 1);
+}
+inline size_t diag_ws_bytes(int batch, int hq, int hkv, int d, int r, int n_splits, int64_t n_ctx) {
+  const int g = hq / hkv;
+  return (diag_ws_q_doubles(batch, hkv, g, d) + diag_ws_qu_doubles(batch, hkv, g, r) +
+          (size_t)batch * hq * n_splits * kDiagPart + (size_t)batch * hkv * (size_t)n_ctx) * sizeof(double);
+}
+
 // Workspace of a decode: per-(b, h) arrival counters (rounded up to 256 bytes), then the split
 // partials (unnormalised outputs, then running max and sum).
 inline size_t decode_ws_counter_bytes(int batch, int hkv) {
@@ -117,6 +165,7 @@ inline size_t decode_ws_bytes(int batch, int hq, int hkv, int d, int n_splits) {
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_mfma_split(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_diagnostics(const DiagArgs& a, hipStream_t stream);
 
 // Host eigensolver used by headq_calibrate (fp64, symmetric). Returns false on non-convergence.
 bool symmetric_eigen(int n, double* A, double* eigenvalues, double* eigenvectors);

@@ -24,7 +24,8 @@ def _header_functions():
 
 def test_library_exports_every_declared_symbol():
     declared = _header_functions()
-    assert declared == sorted(["headq_calibrate", "headq_cache_append", "headq_decode_attn", "headq_status_string"])
+    assert declared == sorted(["headq_calibrate", "headq_cache_append", "headq_decode_attn", "headq_score_diagnostics",
+                               "headq_status_string"])
     out = subprocess.run(["nm", "-D", "--defined-only", str(bd.LIB_PATH)], capture_output=True, text=True,
                          check=True).stdout
     exported = set(re.findall(r" T (headq_\w+)", out))
@@ -200,3 +201,36 @@ def test_decode_workspace_query_and_validation():
     assert _decode_status(cfg, out_dtype=5)[0] == 7
     assert _decode_status(cfg, q=None)[0] == 1
     assert hq.decode_workspace_bytes(cfg, 64, 2) == 256 + 2 * 4 * 2 * 66 * 4
+
+
+def _diag_status(cfg, cache=None, q=0x30000000, k=None, v=None, n_ctx=64, stats=0x40000000, ws=0x50000000,
+                 nbytes=1 << 20, n_splits=0):
+    lib = hq.load()
+    c = cfg.c()
+    cache = _fake_cache(cfg) if cache is None else cache
+    k = _fake_keys(cfg) if k is None else k
+    nb = ctypes.c_size_t(nbytes)
+    ks = (ctypes.c_int64 * 3)(*k._strides[:3])
+    vs = (ctypes.c_int64 * 3)(*v._strides[:3]) if v is not None else None
+    st = lib.headq_score_diagnostics(ctypes.byref(c), ctypes.byref(cache), q, k.addr, ks,
+                                     v.addr if v is not None else None, vs, n_ctx, 1.0, stats, n_splits, ws,
+                                     ctypes.byref(nb), None)
+    return st, nb.value
+
+
+def test_score_diagnostics_workspace_query_and_validation():
+    cfg = _cfg()
+    st, nb = _diag_status(cfg, ws=None, nbytes=0)
+    assert st == 0 and nb > 0
+    st2, nb2 = _diag_status(cfg, ws=None, nbytes=0, n_ctx=128)
+    assert st2 == 0 and nb2 > nb                                              # per-token value errors
+    assert _diag_status(cfg, nbytes=nb - 8)[0] == 5                          # workspace too small
+    assert _diag_status(cfg, n_ctx=48)[0] == 1                               # n_ctx % 32 without tails
+    assert _diag_status(cfg, n_ctx=160)[0] == 4                              # n_ctx > capacity
+    assert _diag_status(cfg, n_ctx=0)[0] == 2
+    assert _diag_status(cfg, n_splits=2)[0] == 2                             # more splits than 64-token chunks
+    assert _diag_status(cfg, q=0x30000004)[0] == 3                           # misaligned query
+    assert _diag_status(cfg, stats=0x40000008)[0] == 3                       # misaligned statistics
+    assert _diag_status(cfg, k=_fake_keys(cfg, align=4))[0] == 3             # misaligned keys
+    assert _diag_status(cfg, stats=None)[0] == 1
+    assert _diag_status(cfg, cache=_paged(cfg, 3, 8))[0] == 2                # paged: capacity > 32 * max_pages
