@@ -6,6 +6,8 @@ Decode workloads (qwen7b_decode, the default; tinyllama_decode; qwen14b_fullkv):
 decode step through libheadq, per layer headq_cache_append of the newest 32-token group of every
 (b, h) stream, then headq_decode_attn over the whole context (tinyllama_decode runs its 22 layers,
 each on its own cache). append_prefill: one step is headq_cache_append of the whole prefill.
+qwen7b_diagnostics: one step is headq_score_diagnostics over the full Qwen2.5-7B-shaped cache
+against the keys and values it was written from (calibration-sweep diagnostics).
 The calibration (host PCA) runs once before timing, as the method prescribes (offline), and is
 reported separately. Inputs are seeded synthetic tensors resident in HBM before timing starts;
 several cache copies are rotated so the 256 MB MALL cannot hold the working set.
@@ -136,6 +138,129 @@ def cpu_baseline(w, U, threads: int, rows: int, cpu_seconds: float = 15.0):
                       f"{w.n_ctx} tokens, {passes} passes ({wall:.2f} s wall, {cpu:.1f} s CPU)"}
 
 
+DIAG_WORKLOADS = {"qwen7b_diagnostics": "qwen7b_decode"}  # diagnostics step over a decode workload's cache
+
+
+def diagnostics_bytes_per_token_head(w) -> int:
+    """Bytes the diagnostics must read per token per KV head: reference keys and values, and the
+    cache's keys (codes, step/zero, side code) and values."""
+    es = {"f32": 4, "bf16": 2}
+    return w.head_dim * (es[w.key_dtype] + es[w.value_dtype]) + algorithmic_bytes_per_token_head(w)
+
+
+def diag_cpu_baseline(w, U, K, V, q, threads: int, streams: int, cpu_seconds: float = 15.0):
+    """The oracle's score_diagnostics (as it stands) on a bounded sample of (b, h) streams."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+
+    from oracle import diagnostics as dg
+    from oracle import oracle as orc
+    from workloads import synth
+
+    g = w.gqa
+    pick = [(b % w.batch, b % w.n_kv_heads) for b in range(streams)]
+    wb = synth.scaled(w, batch=1, n_kv_heads=1, n_q_heads=g)
+
+    def build(bh):
+        b, h = bh
+        oc = orc.empty_cache(1, 1, w.n_ctx, w.head_dim, w.rank, 0, 1)
+        v = (np.ascontiguousarray(V[b, h]).view(np.uint32) >> 16).astype(np.uint16)
+        orc.write_stream(oc, 0, 0, 0, K[b, h], v, U[h], 0, 1)
+        return oc
+
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        caches = list(ex.map(build, pick))
+
+    def one(i):
+        b, h = pick[i]
+        dg.score_diagnostics(caches[i], q[b:b + 1, h * g:(h + 1) * g], U[h:h + 1], wb.n_ctx, 1.0,
+                             K[b:b + 1, h:h + 1], V[b:b + 1, h:h + 1], 0, 1)
+
+    passes, cpu, wall = 0, 0.0, 0.0
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        while passes == 0 or (cpu < cpu_seconds and passes < 64):
+            c0, t0 = time.process_time(), time.perf_counter()
+            list(ex.map(one, range(len(pick))))
+            cpu += time.process_time() - c0
+            wall += time.perf_counter() - t0
+            passes += 1
+    n = passes * len(pick) * g * w.n_ctx
+    return {"value": n / wall, "unit": "query-head cached tokens/s", "cores": min(threads, len(pick)), "kind": "oracle",
+            "sample": f"fp64 oracle score_diagnostics of {len(pick)} (b, h) streams x {g} query heads x "
+                      f"{w.n_ctx} tokens, {passes} passes ({wall:.2f} s wall, {cpu:.1f} s CPU)"}
+
+
+def run_diagnostics(args, hq, synth, torch, np):
+    """One step = headq_score_diagnostics over the whole cache (events on the library's stream)."""
+    w = synth.WORKLOADS[DIAG_WORKLOADS[args.workload]]
+    dev = torch.device("cuda:0")
+    DT = {"f32": hq.HEADQ_F32, "bf16": hq.HEADQ_BF16}
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16}
+    cfg = hq.Config(head_dim=w.head_dim, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads, batch=w.batch,
+                    capacity=w.n_ctx, rank=w.rank, key_dtype=DT[w.key_dtype], value_dtype=DT[w.value_dtype],
+                    value_mode=hq.HEADQ_V_DENSE if w.value_mode == "dense" else hq.HEADQ_V_Q2,
+                    query_dtype=DT[w.query_dtype])
+    U, _ = hq.headq_calibrate(cfg, synth.calibration_queries(w))
+    Kh = synth.stack_streams(w, "keys", workers=16)
+    Vh = synth.stack_streams(w, "values", workers=16)
+    qh = synth.decode_queries(w)
+    K = torch.from_numpy(Kh).to(dev).to(tdt[w.key_dtype])
+    V = torch.from_numpy(Vh).to(dev).to(tdt[w.value_dtype])
+    q = torch.from_numpy(qh).to(dev).to(tdt[w.query_dtype])
+    dc = hq.DeviceCache(cfg, device=dev)
+    dc.set_basis(U)
+    dc.append(K, V, 0)
+    n_ctx = w.n_ctx
+    nb = hq.diagnostics_workspace_bytes(cfg, n_ctx, args.splits)
+    ws = torch.empty((nb + 7) // 8, dtype=torch.float64, device=dev)
+    stats = torch.empty((w.batch, w.n_q_heads, len(hq.DIAG_STATS)), dtype=torch.float64, device=dev)
+    stream = torch.cuda.current_stream()
+    copy_gbs = copy_ceiling(torch, dev, stream)
+
+    def run():
+        hq.headq_score_diagnostics(cfg, dc.c(), q, K, V, n_ctx, stats, 1.0, args.splits, ws, stream)
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        run()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    step_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    ms = float(step_ms.mean())
+    per_tok = diagnostics_bytes_per_token_head(w)
+    alg = per_tok * w.batch * w.n_kv_heads * n_ctx
+    achieved = alg / (ms / 1e3) / 1e9
+    tok_heads = w.batch * w.n_q_heads * n_ctx
+    result = {
+        "metric": "score-diagnostics cached tokens·heads/s + achieved HBM GB/s (% of peak), 1 GPU",
+        "value": tok_heads / (ms / 1e3), "unit": "query-head cached tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f64", "data": "synthetic",
+        "config": {"workload": f"{args.workload}: headq_score_diagnostics (Fisher variance, KL, A^2, entropy) over "
+                               f"the Qwen2.5-7B-shaped cache, Hq {w.n_q_heads}, Hkv {w.n_kv_heads}, d {w.head_dim}, "
+                               f"batch {w.batch}, context {n_ctx}, rank {w.rank}, bf16 reference keys and values",
+                   "batch": w.batch, "n_ctx": n_ctx, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
+                   "head_dim": w.head_dim, "rank": w.rank, "n_splits": args.splits or "auto",
+                   "step": "headq_score_diagnostics (query prep, value errors, stream pass, split merge)"},
+        "roofline": {"bound": "hbm", "kernel": "headq_score_diagnostics (four launches, timed together)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": None, "algorithmic_bytes_per_launch": alg, "bytes_per_token_kv_head": per_tok,
+                     "copy_ceiling_gbs": copy_gbs},
+        "ms_p10_p90": [float(np.percentile(step_ms, 10)), float(np.percentile(step_ms, 90))],
+        "wall_s_timed": wall,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = diag_cpu_baseline(w, U, Kh, Vh, qh, min(16, os.cpu_count() or 1), 16)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -167,6 +292,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+    if args.workload in DIAG_WORKLOADS:
+        run_diagnostics(args, hq, synth, torch, np)
+        return
     dev = torch.device("cuda:0")
     w = synth.WORKLOADS[args.workload]
     DT = {"f32": hq.HEADQ_F32, "bf16": hq.HEADQ_BF16}

@@ -17,7 +17,8 @@
 //   prep    queries and U_h^T q in f64 into the workspace (one workgroup per (b, query head))
 //   value   (with reference values) |v_hat_j - v_j|^2 per token into the workspace
 //   stream  grid (splits, KV heads, batch), 4 waves; a wave takes 64-token chunks (lane = token)
-//           and the stream's query heads in batches of 4. The queries are wave-uniform, so they
+//           and the stream's query heads in batches of 4 (two or four batches: one wave group
+//           each, walking the same chunks together). The queries are wave-uniform, so they
 //           come through scalar loads and every fma takes them as a scalar operand. Each wave
 //           keeps one running max per head, shared by its lanes, so a lane accumulates
 //           e^{s - M}-weighted sums (rescaled when M grows); the wave, then the workgroup, reduce
@@ -127,55 +128,108 @@ __global__ __launch_bounds__(128) void diag_prep_kernel(DiagArgs a) {
   }
 }
 
-// ---- value pass: dv2[b][h][j] = |v_hat_j - v_j|^2 for the A^2 surrogate. A workgroup takes 32
-// tokens of one stream; 8 adjacent threads share a token, each summing d/8 channels.
-template <int D>
+// ---- value pass: dv2[b][h][j] = |v_hat_j - v_j|^2 for the A^2 surrogate. A workgroup takes one
+// 32-token group of one stream. Both tiles are staged in LDS with 16-byte loads in their own layout
+// (reference rows [t][c]; the cache's group block [c][t], 2-bit codes and grid as stored, or the
+// tail rows), values widened to f32 (exact for bf16/f32 and the stored dense values); thread
+// (part, t) then sums d/8 channels of token t, and the 8 partial sums are added in part order.
+template <bool VBF>
+__device__ __forceinline__ float widen(const uint32_t* w, int e) {  // element e of a 16-byte chunk
+  if constexpr (VBF) return __uint_as_float((e % 2 ? w[e / 2] >> 16 : w[e / 2] & 0xffffu) << 16);
+  else return __uint_as_float(w[e]);
+}
+
+template <int D, bool VBF>
 __global__ __launch_bounds__(kThreads) void diag_value_kernel(DiagArgs a) {
-  constexpr int CPT = D / 8;  // channels per thread
-  const int h = blockIdx.y, b = blockIdx.z;
-  const int t = threadIdx.x / 8, part = threadIdx.x % 8;
-  const int64_t j = (int64_t)blockIdx.x * kGroup + t;
+  constexpr int CPT = D / 8;                  // channels per thread
+  constexpr int PR = D + 1, PV = kGroup + 1;  // LDS pitches (floats), bank-conflict free reads
+  __shared__ float ref_s[kGroup][PR];         // reference values [t][c]
+  __shared__ float val_s[D][PV];              // the cache's values [c][t] (dense or tail)
+  __shared__ __attribute__((aligned(16))) uint8_t code_s[D * 8];  // 2-bit: the code block as stored
+  __shared__ __attribute__((aligned(16))) uint16_t meta_s[2 * D];  // 2-bit: step, zero [2][d/32][32]
+  __shared__ double part_s[8][kGroup];
+  const int h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+  const int64_t g0 = (int64_t)blockIdx.x * kGroup;
   const int64_t bh = (int64_t)b * a.hkv + h;
   const int64_t n_full = a.n_ctx / kGroup * kGroup;
-  const bool vbf = a.value_bf16;
-  double e2 = 0.0;
-  if (j < a.n_ctx) {
-    const char* vr = (const char*)a.v_ref + ((int64_t)b * a.vs_b + (int64_t)h * a.vs_h + j * a.vs_t) * (vbf ? 2 : 4);
-    double vh[8], v[8];
-    for (int n = part * CPT / 8; n < (part + 1) * CPT / 8; ++n) {  // 8 channels at a time
-      load8(vr, n, vbf, v);
-      if (j >= n_full) {
-        load8((const char*)a.vtail + (bh * kGroup + j % kGroup) * D * (vbf ? 2 : 4), n, vbf, vh);
-      } else {
-        const int64_t blk = a.map.block(b, h, j / kGroup);
-        const int tt = (int)(j % kGroup);
-        if (a.value_mode == HEADQ_V_DENSE) {
-          const char* vg = (const char*)a.vdense + blk * D * kGroup * (vbf ? 2 : 4);
+  const int n_tok = (int)(a.n_ctx - g0 < kGroup ? a.n_ctx - g0 : kGroup);
+  const bool tail = g0 >= n_full;
+  constexpr int es = VBF ? 2 : 4, epc = 16 / es;  // element size, elements per 16-byte chunk
+  constexpr int chunks_row = D / epc;
+
+  // reference rows (and tail rows) [t][c] -> LDS
+  for (int i = tid; i < kGroup * chunks_row; i += kThreads) {
+    const int t = i / chunks_row, c0 = (i % chunks_row) * epc;
+    float x[8] = {0, 0, 0, 0, 0, 0, 0, 0}, y[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (t < n_tok) {
+      const char* vr = (const char*)a.v_ref + ((int64_t)b * a.vs_b + (int64_t)h * a.vs_h + (g0 + t) * a.vs_t) * es;
+      const uint4 u = *reinterpret_cast<const uint4*>(vr + c0 * es);
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-          for (int i = 0; i < 8; ++i) vh[i] = elem(vg, (int64_t)(8 * n + i) * kGroup + tt, vbf);
-        } else {
-          const uint8_t* vc = a.vcode + blk * D * 8;
-          const uint16_t* vm = a.vmeta + blk * 2 * D;
-          const int gc = 8 * n / 32;
-          const double sv = f16_bits(vm[gc * kGroup + tt]), zv = f16_bits(vm[(D / 32 + gc) * kGroup + tt]);
+      for (int e = 0; e < epc; ++e) x[e] = widen<VBF>(w, e);
+      if (tail) {
+        const char* vt = (const char*)a.vtail + (bh * kGroup + t) * D * es;
+        const uint4 v = *reinterpret_cast<const uint4*>(vt + c0 * es);
+        const uint32_t z[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const uint32_t pair = *(const uint16_t*)(vc + vcode_pair_offset(D, 8 * n + i, tt));
-            vh[i] = (double)((pair >> vcode_pair_bit(tt)) & 3u) * sv + zv;
-          }
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const double dv = vh[i] - v[i];
-        e2 = fma(dv, dv, e2);
+        for (int e = 0; e < epc; ++e) y[e] = widen<VBF>(z, e);
       }
     }
+#pragma unroll
+    for (int e = 0; e < epc; ++e) {
+      ref_s[t][c0 + e] = x[e];
+      if (tail) val_s[c0 + e][t] = y[e];
+    }
   }
-  e2 += __shfl_xor(e2, 1);
-  e2 += __shfl_xor(e2, 2);
-  e2 += __shfl_xor(e2, 4);
-  if (part == 0 && j < a.n_ctx) a.ws_dv2[bh * a.n_ctx + j] = e2;
+  if (!tail) {
+    const int64_t blk = a.map.block(b, h, g0 / kGroup);
+    if (a.value_mode == HEADQ_V_DENSE) {
+      // group block [c][32 tokens]: a chunk is epc tokens of one channel
+      const char* vg = (const char*)a.vdense + blk * D * kGroup * es;
+      for (int i = tid; i < D * kGroup / epc; i += kThreads) {
+        const int c = i / (kGroup / epc), t0 = (i % (kGroup / epc)) * epc;
+        const uint4 u = reinterpret_cast<const uint4*>(vg)[i];
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int e = 0; e < epc; ++e) val_s[c][t0 + e] = widen<VBF>(w, e);
+      }
+    } else {
+      for (int i = tid; i < D * 8 / 16; i += kThreads)
+        reinterpret_cast<uint4*>(code_s)[i] = reinterpret_cast<const uint4*>(a.vcode + blk * D * 8)[i];
+      for (int i = tid; i < 2 * D / 8; i += kThreads)
+        reinterpret_cast<uint4*>(meta_s)[i] = reinterpret_cast<const uint4*>(a.vmeta + blk * 2 * D)[i];
+    }
+  }
+  __syncthreads();
+
+  const int t = tid % kGroup, part = tid / kGroup;
+  const bool q2 = !tail && a.value_mode != HEADQ_V_DENSE;
+  double e2 = 0.0;
+  if (t < n_tok) {
+    const int bit = vcode_pair_bit(t);
+#pragma unroll 8
+    for (int k = 0; k < CPT; ++k) {
+      const int c = part * CPT + k;
+      double vh;
+      if (q2) {
+        const uint32_t pair = *reinterpret_cast<const uint16_t*>(code_s + vcode_pair_offset(D, c, t));
+        const int gc = c / 32;
+        vh = (double)((pair >> bit) & 3u) * f16_bits(meta_s[gc * kGroup + t]) +
+             f16_bits(meta_s[(D / 32 + gc) * kGroup + t]);
+      } else {
+        vh = (double)val_s[c][t];
+      }
+      const double dv = vh - (double)ref_s[t][c];
+      e2 = fma(dv, dv, e2);
+    }
+  }
+  part_s[part][t] = e2;
+  __syncthreads();
+  if (tid < n_tok) {
+    double sum = 0.0;
+    for (int p = 0; p < 8; ++p) sum += part_s[p][tid];
+    a.ws_dv2[bh * a.n_ctx + g0 + tid] = sum;
+  }
 }
 
 // One f64 element of 32 channels held as raw 32-bit words: bf16 pairs or f32.
@@ -199,11 +253,17 @@ __global__ __launch_bounds__(kThreads) void diag_stream_kernel(DiagArgs a) {
   const int64_t bh = (int64_t)b * a.hkv + h;
   const int64_t n_ctx = a.n_ctx, n_full = n_ctx / kGroup * kGroup;
   const int64_t n_chunks = (n_ctx + 63) / 64;
-  const int W = a.n_splits * kWaves;
   const double inv_sqrt_d = 1.0 / sqrt((double)D);
+  // Head batches: with 2 or 4 of them the waves split into groups, one batch per group, that walk
+  // the same chunks together (the second read of a chunk hits the caches); with 1 or 3 every wave
+  // runs the batches in turn.
+  const int nb = (g + kHB - 1) / kHB;
+  const int wpb = kWaves % nb == 0 ? kWaves / nb : kWaves;  // waves per batch
+  const int n_rounds = wpb == kWaves ? nb : 1;
+  const int slot = wave % wpb, W = a.n_splits * wpb;
 
-  for (int hb = 0; hb < g; hb += kHB) {
-    const int nh = g - hb < kHB ? g - hb : kHB;
+  for (int round = 0; round < n_rounds; ++round) {
+    const int hb = (wpb == kWaves ? round : wave / wpb) * kHB;
     // padded heads (past g) have zero queries: every batch runs all kHB heads unconditionally
     const int64_t wrow = ((int64_t)b * a.hkv + h) * diag_padded_heads(g) + hb;
     const const_f64_ptr qh = (const_f64_ptr)(a.ws_q + wrow * D);
@@ -214,7 +274,7 @@ __global__ __launch_bounds__(kThreads) void diag_stream_kernel(DiagArgs a) {
       M[i] = -INFINITY;
       S0[i] = S1[i] = S2[i] = S3[i] = S4[i] = S5[i] = MX[i] = 0.0;
     }
-    for (int64_t k = (int64_t)split * kWaves + wave; k < n_chunks; k += W) {
+    for (int64_t k = (int64_t)split * wpb + slot; k < n_chunks; k += W) {
       const int64_t j = k * 64 + lane;
       const bool valid = j < n_ctx, tail = j >= n_full;
       double acc_s[kHB], acc_d[kHB];
@@ -351,18 +411,20 @@ __global__ __launch_bounds__(kThreads) void diag_stream_kernel(DiagArgs a) {
       }
     }
     __syncthreads();
-    if (threadIdx.x < nh) {
-      const int i = threadIdx.x;
+    // one thread per (wave group, head): merge the group's waves into the split partial
+    const int grp = threadIdx.x / kHB, i = threadIdx.x % kHB;
+    const int hb_t = (wpb == kWaves ? round : grp) * kHB;
+    if (grp < kWaves / wpb && hb_t + i < g) {
       double Mx = -INFINITY;
-      for (int w = 0; w < kWaves; ++w) Mx = fmax(Mx, part_s[w][i][0]);
+      for (int w = grp * wpb; w < (grp + 1) * wpb; ++w) Mx = fmax(Mx, part_s[w][i][0]);
       double acc[6] = {0, 0, 0, 0, 0, 0}, mx = 0.0;
-      for (int w = 0; w < kWaves; ++w) {
+      for (int w = grp * wpb; w < (grp + 1) * wpb; ++w) {
         mx = fmax(mx, part_s[w][i][7]);
         if (part_s[w][i][0] == -INFINITY) continue;
         const double f = exp(part_s[w][i][0] - Mx);
         for (int k = 0; k < 6; ++k) acc[k] = fma(part_s[w][i][1 + k], k == 4 ? f * f : f, acc[k]);
       }
-      double* out = a.ws_part + (((int64_t)b * a.hq + hq0 + hb + i) * a.n_splits + split) * kDiagPart;
+      double* out = a.ws_part + (((int64_t)b * a.hq + hq0 + hb_t + i) * a.n_splits + split) * kDiagPart;
       out[0] = Mx;
       for (int k = 0; k < 6; ++k) out[1 + k] = acc[k];
       out[7] = mx;
@@ -414,7 +476,10 @@ template <int D>
 hipError_t launch_d(const DiagArgs& a, hipStream_t s) {
   if (a.v_ref) {
     dim3 grid((unsigned)((a.n_ctx + kGroup - 1) / kGroup), (unsigned)a.hkv, (unsigned)a.batch);
-    hipLaunchKernelGGL((diag_value_kernel<D>), grid, dim3(kThreads), 0, s, a);
+    if (a.value_bf16)
+      hipLaunchKernelGGL((diag_value_kernel<D, true>), grid, dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((diag_value_kernel<D, false>), grid, dim3(kThreads), 0, s, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
