@@ -300,3 +300,22 @@ def value_rows(cache, b, h, n_ctx, value_mode=0, value_dtype=1):
                                 _p(arrs.get("vmeta")), _p(arrs.get("vtail")), b, h, _p(out)), "value_rows")
     return out
 
+
+def prefill(cache, q, U, start, kappa=1.0, value_mode=0, value_dtype=1):
+    """Chunked-prefill attention over the packed cache: query token t of every batch row sits at
+    position start + t and attends the cached tokens 0 .. start + t (causal), i.e. one fp64
+    decode per query token with n_ctx = start + t + 1 (the summary's §3 step 3 read, per token).
+
+    q: f32 [B][n_q][Hq][d]. Returns (logits f64 [B][n_q][Hq][start + n_q], zero past each token's
+    causal limit; out f64 [B][n_q][Hq][d])."""
+    q = np.ascontiguousarray(q, np.float32)
+    B, n_q, Hq, d = q.shape
+    L = start + n_q
+    logits = np.zeros((B, n_q, Hq, L), np.float64)
+    out = np.zeros((B, n_q, Hq, d), np.float64)
+    for t in range(n_q):
+        lg, o = decode(cache, q[:, t], U, start + t + 1, kappa, value_mode, value_dtype)
+        logits[:, t, :, :start + t + 1] = lg
+        out[:, t] = o
+    return logits, out
+
