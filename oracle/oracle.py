@@ -302,20 +302,30 @@ def value_rows(cache, b, h, n_ctx, value_mode=0, value_dtype=1):
 
 
 def prefill(cache, q, U, start, kappa=1.0, value_mode=0, value_dtype=1):
-    """Chunked-prefill attention over the packed cache: query token t of every batch row sits at
-    position start + t and attends the cached tokens 0 .. start + t (causal), i.e. one fp64
-    decode per query token with n_ctx = start + t + 1 (the summary's §3 step 3 read, per token).
+    """Chunked-prefill attention over the packed cache (the summary's §3 step 3 read, per query
+    token): the cache holds tokens [0, start + n_q) — whole groups packed, the unfinished group
+    exact in the tails — and query token t, at position start + t, attends tokens 0 .. start + t of
+    that cache (causal), with the corrected logits of the oracle decode over the whole cache and
+    the cache's value rows.
 
     q: f32 [B][n_q][Hq][d]. Returns (logits f64 [B][n_q][Hq][start + n_q], zero past each token's
     causal limit; out f64 [B][n_q][Hq][d])."""
     q = np.ascontiguousarray(q, np.float32)
     B, n_q, Hq, d = q.shape
     L = start + n_q
+    Hkv = cache["kcode"].shape[1]
+    g = Hq // Hkv
     logits = np.zeros((B, n_q, Hq, L), np.float64)
     out = np.zeros((B, n_q, Hq, d), np.float64)
+    vrows = {(b, h): value_rows(cache, b, h, L, value_mode, value_dtype) for b in range(B) for h in range(Hkv)}
     for t in range(n_q):
-        lg, o = decode(cache, q[:, t], U, start + t + 1, kappa, value_mode, value_dtype)
-        logits[:, t, :, :start + t + 1] = lg
-        out[:, t] = o
+        lg, _ = decode(cache, q[:, t], U, L, kappa, value_mode, value_dtype)  # every cached token
+        P = start + t
+        for b in range(B):
+            for a in range(Hq):
+                s = lg[b, a, :P + 1]
+                p = np.exp(s - s.max())
+                p /= p.sum()
+                logits[b, t, a, :P + 1] = s
+                out[b, t, a] = p @ vrows[(b, a // g)][:P + 1]
     return logits, out
-
