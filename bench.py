@@ -8,6 +8,8 @@ decode step through libheadq, per layer headq_cache_append of the newest 32-toke
 each on its own cache). append_prefill: one step is headq_cache_append of the whole prefill.
 qwen7b_diagnostics: one step is headq_score_diagnostics over the full Qwen2.5-7B-shaped cache
 against the keys and values it was written from (calibration-sweep diagnostics).
+qwen7b_prefill: one step is headq_prefill_attn of a 512-token chunk at the end of a 16384-token
+Qwen2.5-7B-shaped context (batch 4), the chunk's keys and values already appended.
 The calibration (host PCA) runs once before timing, as the method prescribes (offline), and is
 reported separately. Inputs are seeded synthetic tensors resident in HBM before timing starts;
 several cache copies are rotated so the 256 MB MALL cannot hold the working set.
@@ -191,6 +193,113 @@ def diag_cpu_baseline(w, U, K, V, q, threads: int, streams: int, cpu_seconds: fl
                       f"{w.n_ctx} tokens, {passes} passes ({wall:.2f} s wall, {cpu:.1f} s CPU)"}
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0      # dense bf16 / fp16 matrix peak
+PREFILL_WORKLOADS = {"qwen7b_prefill": ("qwen7b_decode", 4, 512)}  # base shape, batch, chunk tokens
+
+
+def run_prefill(args, hq, synth, torch, np):
+    """One step = headq_prefill_attn of the chunk over the cache (events on the library's stream)."""
+    base, B, n_q = PREFILL_WORKLOADS[args.workload]
+    w = synth.scaled(synth.WORKLOADS[base], batch=B)
+    dev = torch.device("cuda:0")
+    DT = {"f32": hq.HEADQ_F32, "bf16": hq.HEADQ_BF16}
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16}
+    cfg = hq.Config(head_dim=w.head_dim, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads, batch=B,
+                    capacity=w.n_ctx, rank=w.rank, key_dtype=DT[w.key_dtype], value_dtype=DT[w.value_dtype],
+                    value_mode=hq.HEADQ_V_DENSE if w.value_mode == "dense" else hq.HEADQ_V_Q2,
+                    query_dtype=DT[w.query_dtype])
+    U, _ = hq.headq_calibrate(cfg, synth.calibration_queries(w))
+    K = torch.from_numpy(synth.stack_streams(w, "keys", workers=16)).to(dev).to(tdt[w.key_dtype])
+    V = torch.from_numpy(synth.stack_streams(w, "values", workers=16)).to(dev).to(tdt[w.value_dtype])
+    start = w.n_ctx - n_q
+    qh = synth.decode_queries(w, batch=B * n_q, stream=7).reshape(B, n_q, w.n_q_heads, w.head_dim)
+    q = torch.from_numpy(np.ascontiguousarray(qh)).to(dev).to(tdt[w.query_dtype])
+    dc = hq.DeviceCache(cfg, device=dev)
+    dc.set_basis(U)
+    dc.append(K, V, 0)
+    del K, V
+    out = torch.empty((B, n_q, w.n_q_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def run():
+        hq.headq_prefill_attn(cfg, dc.c(), q, start, out, hq.HEADQ_BF16, 1.0, None, stream)
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        run()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    step_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    ms = float(step_ms.mean())
+    # algorithmic work: q.k and p.v over every attended (query token, head, cached token)
+    attended = sum(start + t + 1 for t in range(n_q))
+    flops = 2 * 2 * w.head_dim * w.n_q_heads * B * attended
+    achieved = flops / (ms / 1e3) / 1e12
+    result = {
+        "metric": "chunked-prefill attention query·cached-token pairs/s + achieved matrix TFLOP/s, 1 GPU",
+        "value": w.n_q_heads * B * attended / (ms / 1e3), "unit": "query-head·cached-token pairs/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16/bf16 operands (hi+lo), f32 accumulate", "data": "synthetic",
+        "config": {"workload": f"{args.workload}: headq_prefill_attn of a {n_q}-token chunk at positions "
+                               f"{start}..{w.n_ctx - 1} over the Qwen2.5-7B-shaped HeadQ cache, Hq {w.n_q_heads}, "
+                               f"Hkv {w.n_kv_heads}, d {w.head_dim}, batch {B}, rank {w.rank}, dense bf16 values",
+                   "batch": B, "n_q": n_q, "start": start, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
+                   "head_dim": w.head_dim, "rank": w.rank, "step": "headq_prefill_attn (one launch)"},
+        "roofline": {"bound": "mfma", "kernel": "prefill_mfma_kernel (one launch)", "achieved": achieved,
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+                     "traffic": None, "algorithmic_flops_per_launch": flops,
+                     "note": "every f32 factor is contracted as a high and a low half-precision part, so the "
+                             "matrix cores execute at least twice the algorithmic flops"},
+        "ms_p10_p90": [float(np.percentile(step_ms, 10)), float(np.percentile(step_ms, 90))],
+        "wall_s_timed": wall,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = prefill_cpu_baseline(w, U, start, n_q, qh, min(16, os.cpu_count() or 1))
+    print(json.dumps(result), flush=True)
+
+
+def prefill_cpu_baseline(w, U, start, n_q, qh, threads: int, cpu_seconds: float = 15.0):
+    """The oracle's prefill (as it stands) on a bounded sample: one batch row, a few query tokens."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+
+    from oracle import oracle as orc
+    from workloads import synth
+
+    L = start + n_q
+    wb = synth.scaled(w, batch=1)
+    oc = orc.empty_cache(1, w.n_kv_heads, w.n_ctx, w.head_dim, w.rank, 0, 1)
+    for h in range(w.n_kv_heads):
+        k, v = synth.keys(wb, 0, h, L), synth.values(wb, 0, h, L)
+        orc.write_stream(oc, 0, h, 0, k, (v.view(np.uint32) >> 16).astype(np.uint16), U[h], 0, 1)
+    q1 = qh[:1]
+    picks = list(range(n_q - 1, -1, -max(1, n_q // 16)))[:16]
+
+    def one(t):
+        orc.prefill(oc, q1, U, start, 1.0, 0, 1, tokens=[t])
+
+    passes, cpu, wall = 0, 0.0, 0.0
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        while passes == 0 or (cpu < cpu_seconds and passes < 64):
+            c0, t0 = time.process_time(), time.perf_counter()
+            list(ex.map(one, picks))
+            cpu += time.process_time() - c0
+            wall += time.perf_counter() - t0
+            passes += 1
+    pairs = passes * sum(start + t + 1 for t in picks) * w.n_q_heads
+    return {"value": pairs / wall, "unit": "query-head·cached-token pairs/s", "cores": min(threads, len(picks)),
+            "kind": "oracle",
+            "sample": f"fp64 oracle prefill of {len(picks)} query tokens of batch row 0 x {w.n_q_heads} heads over "
+                      f"the {L}-token cache, {passes} passes ({wall:.2f} s wall, {cpu:.1f} s CPU)"}
+
+
 def run_diagnostics(args, hq, synth, torch, np):
     """One step = headq_score_diagnostics over the whole cache (events on the library's stream)."""
     w = synth.WORKLOADS[DIAG_WORKLOADS[args.workload]]
@@ -294,6 +403,9 @@ def main():
     torch.cuda.set_device(0)
     if args.workload in DIAG_WORKLOADS:
         run_diagnostics(args, hq, synth, torch, np)
+        return
+    if args.workload in PREFILL_WORKLOADS:
+        run_prefill(args, hq, synth, torch, np)
         return
     dev = torch.device("cuda:0")
     w = synth.WORKLOADS[args.workload]

@@ -201,6 +201,27 @@ headq_status headq_decode_attn(const headq_config* cfg, const headq_cache* cache
                                float* logits_dbg,
                                int32_t n_splits, void* ws, size_t* ws_bytes, void* stream);
 
+/*
+ * headq_prefill_attn — chunked-prefill attention over the cache: query token t of every batch row
+ * sits at position start + t and attends the cached tokens 0 .. start + t (causal), with the
+ * decode's corrected logit and readout (Summary §3 step 3, read once per query token; §1, §2.2).
+ * The chunk's own keys and values must be in the cache already (headq_cache_append of tokens
+ * [start, start + n_q) first), so the cache holds tokens [0, start + n_q); those past the last
+ * whole group come from ktail / vtail, exactly. Runs on the matrix cores: dense bf16 or 2-bit
+ * values (dense f32 values: UNSUPPORTED). Numerics as headq_decode_attn.
+ *   q           device [B][n_q][Hq][d] in query_dtype (contiguous)
+ *   start, n_q  first position and number of query tokens, start + n_q <= capacity
+ *   out         device [B][n_q][Hq][d] in out_dtype (HEADQ_F32 or HEADQ_BF16), contiguous
+ *   corr_scale  multiplies the correction (1 = HeadQ, 0 = base only, -1 = wrong sign)
+ *   logits_dbg  device f32 [B][n_q][Hq][start + n_q]: logits of the attended tokens (natural-log
+ *               units; entries past a token's causal limit are left untouched), or NULL
+ * Errors: NULL (also: start + n_q not a multiple of 32 without both tails), SHAPE, ALIGN,
+ * CAPACITY, UNSUPPORTED, HIP.
+ */
+headq_status headq_prefill_attn(const headq_config* cfg, const headq_cache* cache, const void* q, int64_t start,
+                                int64_t n_q, void* out, int32_t out_dtype, float corr_scale, float* logits_dbg,
+                                void* stream);
+
 /* Statistics of headq_score_diagnostics, per (batch row, query head). */
 enum {
   HEADQ_DIAG_FISHER_VAR = 0, /* Var_p(ds): Fisher-weighted variance of the score error */

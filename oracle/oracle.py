@@ -301,7 +301,7 @@ def value_rows(cache, b, h, n_ctx, value_mode=0, value_dtype=1):
     return out
 
 
-def prefill(cache, q, U, start, kappa=1.0, value_mode=0, value_dtype=1):
+def prefill(cache, q, U, start, kappa=1.0, value_mode=0, value_dtype=1, tokens=None):
     """Chunked-prefill attention over the packed cache (the summary's §3 step 3 read, per query
     token): the cache holds tokens [0, start + n_q) — whole groups packed, the unfinished group
     exact in the tails — and query token t, at position start + t, attends tokens 0 .. start + t of
@@ -309,7 +309,8 @@ def prefill(cache, q, U, start, kappa=1.0, value_mode=0, value_dtype=1):
     the cache's value rows.
 
     q: f32 [B][n_q][Hq][d]. Returns (logits f64 [B][n_q][Hq][start + n_q], zero past each token's
-    causal limit; out f64 [B][n_q][Hq][d])."""
+    causal limit; out f64 [B][n_q][Hq][d]); with `tokens`, only those query tokens are computed
+    (the others stay zero)."""
     q = np.ascontiguousarray(q, np.float32)
     B, n_q, Hq, d = q.shape
     L = start + n_q
@@ -318,7 +319,7 @@ def prefill(cache, q, U, start, kappa=1.0, value_mode=0, value_dtype=1):
     logits = np.zeros((B, n_q, Hq, L), np.float64)
     out = np.zeros((B, n_q, Hq, d), np.float64)
     vrows = {(b, h): value_rows(cache, b, h, L, value_mode, value_dtype) for b in range(B) for h in range(Hkv)}
-    for t in range(n_q):
+    for t in (range(n_q) if tokens is None else tokens):
         lg, _ = decode(cache, q[:, t], U, L, kappa, value_mode, value_dtype)  # every cached token
         P = start + t
         for b in range(B):

@@ -23,8 +23,8 @@ STATUS = {
     0: "HEADQ_OK", 1: "HEADQ_ERR_NULL", 2: "HEADQ_ERR_SHAPE", 3: "HEADQ_ERR_ALIGN", 4: "HEADQ_ERR_CAPACITY",
     5: "HEADQ_ERR_WORKSPACE", 6: "HEADQ_ERR_NUMERIC", 7: "HEADQ_ERR_UNSUPPORTED", 8: "HEADQ_ERR_HIP",
 }
-EXPORTS = ("headq_calibrate", "headq_cache_append", "headq_decode_attn", "headq_score_diagnostics",
-           "headq_status_string")
+EXPORTS = ("headq_calibrate", "headq_cache_append", "headq_decode_attn", "headq_prefill_attn",
+           "headq_score_diagnostics", "headq_status_string")
 DIAG_STATS = ("fisher_var", "kl", "mean_ds", "max_abs_ds", "a2", "entropy")  # HEADQ_DIAG_* order
 
 
@@ -68,9 +68,11 @@ def load() -> ctypes.CDLL:
         L.headq_cache_append.argtypes = [P, P, P, P, P, P, I64, I64, P, P]
         L.headq_decode_attn.argtypes = [P, P, P, I64, P, P, I32, F, P, I32, P, P, P]
         L.headq_score_diagnostics.argtypes = [P, P, P, P, P, P, P, I64, F, P, I32, P, P, P]
+        L.headq_prefill_attn.argtypes = [P, P, P, I64, I64, P, I32, F, P, P]
         L.headq_status_string.argtypes = [ctypes.c_int]
         L.headq_status_string.restype = ctypes.c_char_p
-        for fn in ("headq_calibrate", "headq_cache_append", "headq_decode_attn", "headq_score_diagnostics"):
+        for fn in ("headq_calibrate", "headq_cache_append", "headq_decode_attn", "headq_prefill_attn",
+                   "headq_score_diagnostics"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -178,6 +180,17 @@ def headq_decode_attn(cfg: Config, cache: headq_cache, q, n_ctx: int, out, out_d
                                     _stream(stream)), "headq_decode_attn")
 
 
+def headq_prefill_attn(cfg: Config, cache: headq_cache, q, start: int, out, out_dtype: int = HEADQ_F32,
+                       corr_scale: float = 1.0, logits_dbg=None, stream=None):
+    """Chunked-prefill attention: q [B][n_q][Hq][d] (torch device tensor, query dtype), query token
+    t at position start + t attending cached tokens 0 .. start + t; out [B][n_q][Hq][d];
+    logits_dbg: optional f32 [B][n_q][Hq][start + n_q]."""
+    c = cfg.c()
+    _check(load().headq_prefill_attn(ctypes.byref(c), ctypes.byref(cache), _ptr(q), start, q.shape[1], _ptr(out),
+                                     out_dtype, float(corr_scale), _ptr(logits_dbg), _stream(stream)),
+           "headq_prefill_attn")
+
+
 def diagnostics_workspace_bytes(cfg: Config, n_ctx: int, n_splits: int = 0) -> int:
     c = cfg.c()
     nbytes = ctypes.c_size_t(0)
@@ -252,6 +265,15 @@ class DeviceCache:
             ws = torch.zeros((nb + 3) // 4, dtype=torch.float32, device=q.device)
         headq_decode_attn(self.cfg, self.c(), q, n_ctx, out, out_dtype, corr_scale, logits_dbg, n_splits, ws, stream,
                           row_len)
+        return out
+
+    def prefill(self, q, start: int, out=None, out_dtype: int = HEADQ_F32, corr_scale: float = 1.0,
+                logits_dbg=None, stream=None):
+        import torch
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32 if out_dtype == HEADQ_F32 else torch.bfloat16,
+                              device=q.device)
+        headq_prefill_attn(self.cfg, self.c(), q, start, out, out_dtype, corr_scale, logits_dbg, stream)
         return out
 
     def score_diagnostics(self, q, k_ref, v_ref, n_ctx: int, corr_scale: float = 1.0, n_splits: int = 0, ws=None,

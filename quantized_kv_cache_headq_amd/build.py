@@ -16,7 +16,8 @@ CSRC = PKG / "csrc"
 OUT = PKG / "libheadq.so"
 BUILD_DIR = PKG / "_build"
 
-SOURCES = ["headq_api.cpp", "calibrate.cpp", "append.hip", "decode.hip", "decode_mfma.hip", "diagnostics.hip"]
+SOURCES = ["headq_api.cpp", "calibrate.cpp", "append.hip", "decode.hip", "decode_mfma.hip", "diagnostics.hip",
+           "prefill_mfma.hip"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

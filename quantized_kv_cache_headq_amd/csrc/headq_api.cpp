@@ -350,3 +350,53 @@ extern "C" headq_status headq_score_diagnostics(const headq_config* cfg, const h
   hipStream_t s = (hipStream_t)stream;
   return finish(headq::launch_diagnostics(a, s), s);
 }
+
+extern "C" headq_status headq_prefill_attn(const headq_config* cfg, const headq_cache* cache, const void* q,
+                                           int64_t start, int64_t n_q, void* out, int32_t out_dtype,
+                                           float corr_scale, float* logits_dbg, void* stream) {
+  headq_status st = check_config(cfg);
+  if (st != HEADQ_OK) return st;
+  if (!cache || !q || !out) return HEADQ_ERR_NULL;
+  st = check_cache(cfg, cache);
+  if (st != HEADQ_OK) return st;
+  if (start < 0 || n_q < 1) return HEADQ_ERR_SHAPE;
+  if (start + n_q > cfg->capacity) return HEADQ_ERR_CAPACITY;
+  if (out_dtype != HEADQ_F32 && out_dtype != HEADQ_BF16) return HEADQ_ERR_UNSUPPORTED;
+  // the matrix-core formats: dense bf16 or 2-bit values
+  if (cfg->value_mode == HEADQ_V_DENSE && cfg->value_dtype != HEADQ_BF16) return HEADQ_ERR_UNSUPPORTED;
+  if ((start + n_q) % headq::kGroup && (!cache->ktail || !cache->vtail)) return HEADQ_ERR_NULL;
+  if (!aligned16(q) || !aligned16(out) || (logits_dbg && !aligned16(logits_dbg))) return HEADQ_ERR_ALIGN;
+
+  headq::PrefillArgs a{};
+  a.d = cfg->head_dim;
+  a.r = cfg->rank;
+  a.hq = cfg->n_q_heads;
+  a.hkv = cfg->n_kv_heads;
+  a.batch = cfg->batch;
+  a.gqa = cfg->n_q_heads / cfg->n_kv_heads;
+  a.cap = cfg->capacity;
+  a.start = start;
+  a.n_q = n_q;
+  a.query_bf16 = cfg->query_dtype == HEADQ_BF16;
+  a.key_bf16 = cfg->key_dtype == HEADQ_BF16;
+  a.value_bf16 = cfg->value_dtype == HEADQ_BF16;
+  a.value_mode = cfg->value_mode;
+  a.out_bf16 = out_dtype == HEADQ_BF16;
+  a.corr_scale = corr_scale;
+  a.q = q;
+  a.kcode = cache->kcode;
+  a.kmeta = cache->kmeta;
+  a.scode = cache->scode;
+  a.ssc = cache->ssc;
+  a.vdense = cache->v;
+  a.vcode = cache->vcode;
+  a.vmeta = cache->vmeta;
+  a.U = cache->U;
+  a.ktail = cache->ktail;
+  a.vtail = cache->vtail;
+  a.map = map_of(cfg, cache);
+  a.logits_dbg = logits_dbg;
+  a.out = out;
+  hipStream_t s = (hipStream_t)stream;
+  return finish(headq::launch_prefill(a, s), s);
+}

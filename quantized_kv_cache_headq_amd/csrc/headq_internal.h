@@ -153,6 +153,29 @@ inline size_t diag_ws_bytes(int batch, int hq, int hkv, int d, int r, int n_spli
           (size_t)batch * hq * n_splits * kDiagPart + (size_t)batch * hkv * (size_t)n_ctx) * sizeof(double);
 }
 
+struct PrefillArgs {
+  int d, r, hq, hkv, batch, gqa;
+  int64_t cap;
+  int64_t start, n_q;          // query token t sits at position start + t; the cache holds
+                               // tokens [0, start + n_q) (whole groups, the rest in the tails)
+  int query_bf16, key_bf16, value_bf16, value_mode, out_bf16;
+  float corr_scale;
+  const void* q;               // [B][n_q][Hq][d]
+  const uint8_t* kcode;
+  const uint16_t* kmeta;
+  const uint8_t* scode;
+  const uint16_t* ssc;
+  const void* vdense;
+  const uint8_t* vcode;
+  const uint16_t* vmeta;
+  const float* U;
+  const void* ktail;
+  const void* vtail;
+  CacheMap map;
+  float* logits_dbg;           // [B][n_q][Hq][start + n_q] or null
+  void* out;                   // [B][n_q][Hq][d]
+};
+
 // Workspace of a decode: per-(b, h) arrival counters (rounded up to 256 bytes), then the split
 // partials (unnormalised outputs, then running max and sum).
 inline size_t decode_ws_counter_bytes(int batch, int hkv) {
@@ -166,6 +189,7 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_mfma_split(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_diagnostics(const DiagArgs& a, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
 // Host eigensolver used by headq_calibrate (fp64, symmetric). Returns false on non-convergence.
 bool symmetric_eigen(int n, double* A, double* eigenvalues, double* eigenvectors);

@@ -24,8 +24,8 @@ def _header_functions():
 
 def test_library_exports_every_declared_symbol():
     declared = _header_functions()
-    assert declared == sorted(["headq_calibrate", "headq_cache_append", "headq_decode_attn", "headq_score_diagnostics",
-                               "headq_status_string"])
+    assert declared == sorted(["headq_calibrate", "headq_cache_append", "headq_decode_attn", "headq_prefill_attn",
+                               "headq_score_diagnostics", "headq_status_string"])
     out = subprocess.run(["nm", "-D", "--defined-only", str(bd.LIB_PATH)], capture_output=True, text=True,
                          check=True).stdout
     exported = set(re.findall(r" T (headq_\w+)", out))
@@ -234,3 +234,25 @@ def test_score_diagnostics_workspace_query_and_validation():
     assert _diag_status(cfg, k=_fake_keys(cfg, align=4))[0] == 3             # misaligned keys
     assert _diag_status(cfg, stats=None)[0] == 1
     assert _diag_status(cfg, cache=_paged(cfg, 3, 8))[0] == 2                # paged: capacity > 32 * max_pages
+
+
+def _prefill_status(cfg, cache=None, q=0x30000000, start=32, n_q=64, out=0x40000000, out_dtype=0, logits=None):
+    lib = hq.load()
+    c = cfg.c()
+    cache = _fake_cache(cfg) if cache is None else cache
+    return lib.headq_prefill_attn(ctypes.byref(c), ctypes.byref(cache), q, start, n_q, out, out_dtype, 1.0, logits,
+                                  None)
+
+
+def test_prefill_validation_statuses():
+    cfg = _cfg(value_dtype=bd.HEADQ_BF16)                                # capacity 128
+    assert _prefill_status(cfg, n_q=0) == 2
+    assert _prefill_status(cfg, start=-1) == 2
+    assert _prefill_status(cfg, start=100, n_q=29) == 4                  # past the capacity
+    assert _prefill_status(cfg, start=3) == 1                            # ends inside a group, no tails
+    assert _prefill_status(_cfg(), start=32) == 7                        # dense f32 values: not a matrix-core format
+    assert _prefill_status(cfg, q=0x30000004) == 3
+    assert _prefill_status(cfg, logits=0x50000008) == 3
+    assert _prefill_status(cfg, out_dtype=3) == 7
+    assert _prefill_status(cfg, q=None) == 1
+    assert _prefill_status(cfg, cache=_paged(cfg, 3, 8)) == 2            # paged: capacity > 32 * max_pages
