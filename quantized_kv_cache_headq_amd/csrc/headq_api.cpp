@@ -359,7 +359,7 @@ extern "C" headq_status headq_prefill_attn(const headq_config* cfg, const headq_
   if (!cache || !q || !out) return HEADQ_ERR_NULL;
   st = check_cache(cfg, cache);
   if (st != HEADQ_OK) return st;
-  if (start < 0 || n_q < 1) return HEADQ_ERR_SHAPE;
+  if (start < 0 || n_q < 1 || start + n_q > INT32_MAX) return HEADQ_ERR_SHAPE;  // positions are 32-bit in-kernel
   if (start + n_q > cfg->capacity) return HEADQ_ERR_CAPACITY;
   if (out_dtype != HEADQ_F32 && out_dtype != HEADQ_BF16) return HEADQ_ERR_UNSUPPORTED;
   // the matrix-core formats: dense bf16 or 2-bit values

@@ -79,8 +79,8 @@ struct Fixed {
 
 // One staged group against the wave's 16 columns: scores, causal mask, online softmax, P.V.
 template <int D, int R, bool VQ2>
-__device__ __forceinline__ void group_step(const uint8_t* T, const Fixed<D, R>& f, float kappa, int64_t tok0,
-                                           bool masked, int64_t n_att, float* lg_row, int n, int quad, int lane,
+__device__ __forceinline__ void group_step(const uint8_t* T, const Fixed<D, R>& f, float kappa, int tok0,
+                                           bool masked, int n_att, float* lg_row, int n, int quad, int lane,
                                            floatx4* o_acc, float* z_acc, float& m_run, float& l_run) {
   using TL = Tile<D, R, VQ2>;
   constexpr int NKT = D / 32, NCT = D / 16, NG = D / 32;
@@ -187,11 +187,15 @@ __device__ __forceinline__ void group_step(const uint8_t* T, const Fixed<D, R>& 
       for (int cg = 0; cg < NG; ++cg) z_acc[cg] *= alpha;
   }
   float p[8];
+  if (masked) {  // a column whose limit falls in this group may see only masked scores (m_run = -inf)
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    p[j] = sv[j] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(sv[j] - m_run);
-    l_run += p[j];
+    for (int j = 0; j < 8; ++j) p[j] = sv[j] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(sv[j] - m_run);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(sv[j] - m_run);
   }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) l_run += p[j];
   if constexpr (VQ2) {
     // v_hat = code * s + z per (token, 32-channel group): the code part is a matrix product with
     // p o s as the second operand (one per channel group); the zero part sum_j p_j z_j per column
@@ -476,8 +480,9 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
     if (gi + 1 < G) fetch_group(gi + 1);  // in flight while this group is computed
     const int64_t tok0 = gi * kGroup;
     if (tok0 < att_max_w)
-      group_step<D, R, VQ2>(reinterpret_cast<const uint8_t*>(tile_s[cur]), f, a.corr_scale, tok0,
-                            tok0 + kGroup > att_min_w, n_att, lg_row, n, quad, lane, o_acc, z_acc, m_run, l_run);
+      group_step<D, R, VQ2>(reinterpret_cast<const uint8_t*>(tile_s[cur]), f, a.corr_scale, (int)tok0,
+                            tok0 + kGroup > att_min_w, (int)n_att, lg_row, n, quad, lane, o_acc, z_acc, m_run,
+                            l_run);
     if (gi + 1 < G) stage_group(cur ^ 1);
     __syncthreads();
   }
