@@ -39,6 +39,8 @@ TRAFFIC = {
     "qwen14b_fullkv": ("decode_qwen14b_fullkv_traffic.json", "decode_mfma.hip"),
     "tinyllama_decode": ("decode_tinyllama_traffic.json", "decode_mfma.hip"),
     "append_prefill": ("append_prefill_traffic.json", "append.hip"),
+    "qwen7b_diagnostics": ("diagnostics_qwen7b_traffic.json", "diagnostics.hip"),
+    "qwen7b_prefill": ("prefill_qwen7b_traffic.json", "prefill_mfma.hip"),
 }
 
 
@@ -75,6 +77,15 @@ def copy_ceiling(torch, dev, stream) -> float:
     gbs = 10 * 2 * src.numel() * 4 / (e0.elapsed_time(e1) / 1e3) / 1e9
     del src, dst
     return gbs
+
+
+def copy_probe(torch, dev):
+    """One 1 GiB device copy: the known-size reference that scales the HBM counters."""
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def source_sha(src: str) -> str:
@@ -220,6 +231,8 @@ def run_prefill(args, hq, synth, torch, np):
     del K, V
     out = torch.empty((B, n_q, w.n_q_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
+    if args.copy_probe:
+        copy_probe(torch, dev)
 
     def run():
         hq.headq_prefill_attn(cfg, dc.c(), q, start, out, hq.HEADQ_BF16, 1.0, None, stream)
@@ -253,7 +266,7 @@ def run_prefill(args, hq, synth, torch, np):
                    "head_dim": w.head_dim, "rank": w.rank, "step": "headq_prefill_attn (one launch)"},
         "roofline": {"bound": "mfma", "kernel": "prefill_mfma_kernel (one launch)", "achieved": achieved,
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
-                     "traffic": None, "algorithmic_flops_per_launch": flops,
+                     "traffic": traffic_per_launch(args.workload), "algorithmic_flops_per_launch": flops,
                      "note": "every f32 factor is contracted as a high and a low half-precision part, so the "
                              "matrix cores execute at least twice the algorithmic flops"},
         "ms_p10_p90": [float(np.percentile(step_ms, 10)), float(np.percentile(step_ms, 90))],
@@ -326,6 +339,8 @@ def run_diagnostics(args, hq, synth, torch, np):
     stats = torch.empty((w.batch, w.n_q_heads, len(hq.DIAG_STATS)), dtype=torch.float64, device=dev)
     stream = torch.cuda.current_stream()
     copy_gbs = copy_ceiling(torch, dev, stream)
+    if args.copy_probe:
+        copy_probe(torch, dev)
 
     def run():
         hq.headq_score_diagnostics(cfg, dc.c(), q, K, V, n_ctx, stats, 1.0, args.splits, ws, stream)
@@ -360,7 +375,8 @@ def run_diagnostics(args, hq, synth, torch, np):
                    "step": "headq_score_diagnostics (query prep, value errors, stream pass, split merge)"},
         "roofline": {"bound": "hbm", "kernel": "headq_score_diagnostics (four launches, timed together)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None, "algorithmic_bytes_per_launch": alg, "bytes_per_token_kv_head": per_tok,
+                     "traffic": traffic_per_launch(args.workload), "algorithmic_bytes_per_launch": alg,
+                     "bytes_per_token_kv_head": per_tok,
                      "copy_ceiling_gbs": copy_gbs},
         "ms_p10_p90": [float(np.percentile(step_ms, 10)), float(np.percentile(step_ms, 90))],
         "wall_s_timed": wall,
