@@ -321,6 +321,22 @@ int orc_pack_kcode(int d, int64_t T, const uint8_t* codes, uint8_t* kcode) {
   return 0;
 }
 
+/* 3- and 4-bit base codes, one per nibble: a token row is d/2 bytes, d/8 little-endian words;
+ * channel 8m + j sits in word m at bit 4*(j/2) + 16*(j%2) (channels 2i and 2i+1 at the same
+ * nibble of the low and the high 16-bit half). */
+static int kcode4_bit(int j) { return 4 * (j / 2) + 16 * (j % 2); }
+
+int orc_pack_kcode4(int d, int64_t T, const uint8_t* codes, uint8_t* kcode) {
+  if (d % 8 || !codes || !kcode) return -1;
+  for (int64_t t = 0; t < T; ++t)
+    for (int m = 0; m < d / 8; ++m) {
+      uint32_t word = 0;
+      for (int j = 0; j < 8; ++j) word |= (uint32_t)(codes[t * d + 8 * m + j] & 15u) << kcode4_bit(j);
+      for (int k = 0; k < 4; ++k) kcode[t * (d / 2) + 4 * m + k] = (uint8_t)(word >> (8 * k));
+    }
+  return 0;
+}
+
 int orc_pack_kmeta(int d, int64_t T, const uint16_t* scale, const uint16_t* zero, uint16_t* kmeta) {
   if (T % GROUP || !scale || !zero || !kmeta) return -1;
   for (int64_t g = 0; g < T / GROUP; ++g)
@@ -397,9 +413,15 @@ int orc_pack_vmeta(int d, int64_t T, const uint16_t* scale, const uint16_t* zero
  * query head hq reads KV head hq / g; every one of the n_ctx cached tokens is attended (no mask);
  * kappa multiplies the correction (1 = HeadQ, 0 = base only, -1 = the wrong-sign control). */
 
-static double k_hat(const uint8_t* kcode_t, const uint16_t* kmeta_g, int d, int c) {
-  const int m = c / 16, j = c % 16, bit = kcode_bit(j);
-  unsigned code = (kcode_t[4 * m + bit / 8] >> (bit % 8)) & 3u;
+static double k_hat(const uint8_t* kcode_t, const uint16_t* kmeta_g, int d, int c, int base_bits) {
+  unsigned code;
+  if (base_bits == 2) {
+    const int m = c / 16, j = c % 16, bit = kcode_bit(j);
+    code = (kcode_t[4 * m + bit / 8] >> (bit % 8)) & 3u;
+  } else {  /* 3 or 4 bits, one code per nibble */
+    const int m = c / 8, j = c % 8, bit = kcode4_bit(j);
+    code = (kcode_t[4 * m + bit / 8] >> (bit % 8)) & 15u;
+  }
   double s = orc_f16_to_f32(kmeta_g[c]);
   double z = orc_f16_to_f32(kmeta_g[d + c]);
   return (double)code * s + z;
@@ -430,10 +452,12 @@ int orc_decode(int d, int hq, int hkv, int r, int value_mode, int value_dtype, i
                int64_t n_ctx, const uint8_t* kcode, const uint16_t* kmeta, const uint8_t* scode,
                const uint16_t* ssc, const void* vdense, const uint8_t* vcode, const uint16_t* vmeta,
                int key_dtype, const void* ktail, const void* vtail, const float* U, const float* q, double kappa,
-               int b_begin, int b_end, double* logits, double* out) {
+               int b_begin, int b_end, double* logits, double* out, int base_bits) {
   if (d <= 0 || d % 4 || hq <= 0 || hkv <= 0 || hq % hkv || r < 0 || r % 2 || cap % GROUP || n_ctx <= 0 ||
-      n_ctx > cap || b_begin < 0 || b_end > B || b_begin > b_end || !kcode || !kmeta || !q || !out)
+      n_ctx > cap || b_begin < 0 || b_end > B || b_begin > b_end || !kcode || !kmeta || !q || !out ||
+      base_bits < 2 || base_bits > 4)
     return -1;
+  const int row_bytes = base_bits == 2 ? d / 4 : d / 2;  /* packed key codes per token */
   /* tokens past the last whole group are the stream's dense tail: exact keys and values */
   const int64_t n_full = n_ctx / GROUP * GROUP;
   if (n_full < n_ctx && (!ktail || !vtail)) return -1;
@@ -466,10 +490,10 @@ int orc_decode(int d, int hq, int hkv, int r, int value_mode, int value_dtype, i
         if (s[j] > smax) smax = s[j];
       }
       for (int64_t j = 0; j < n_full; ++j) {
-        const uint8_t* kt = kcode + (bh * cap + j) * (d / 4);
+        const uint8_t* kt = kcode + (bh * cap + j) * row_bytes;
         const uint16_t* mg = kmeta + (bh * (cap / GROUP) + j / GROUP) * 2 * d;
         double base = 0.0;
-        for (int c = 0; c < d; ++c) base += qd[c] * k_hat(kt, mg, d, c);
+        for (int c = 0; c < d; ++c) base += qd[c] * k_hat(kt, mg, d, c, base_bits);
         double corr = 0.0;
         if (r) {
           double sg = orc_f16_to_f32(ssc[bh * cap + j]);

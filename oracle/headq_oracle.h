@@ -71,6 +71,9 @@ int orc_quantize_values(int d, int bits, int64_t T, const float* v, uint8_t* cod
  *         in byte b of the tile's pair at bits 4e + 2q
  *   vmeta [T/32][2][d/32][32]: row 0 = scale, row 1 = zero, token-minor */
 int orc_pack_kcode(int d, int64_t T, const uint8_t* codes, uint8_t* kcode);
+/*   kcode4 [T][d/2] (d % 8 == 0), 3- and 4-bit base codes one per nibble: d/8 little-endian words
+ *         per token; channel 8m + j in word m at bit 4*(j/2) + 16*(j%2) */
+int orc_pack_kcode4(int d, int64_t T, const uint8_t* codes, uint8_t* kcode);
 int orc_pack_kmeta(int d, int64_t T, const uint16_t* scale, const uint16_t* zero, uint16_t* kmeta);
 int orc_pack_scode(int r, int64_t T, const int8_t* zc, uint8_t* scode);
 int orc_pack_vdense(int d, int64_t T, int elem_bytes, const void* v, void* vdense);
@@ -85,12 +88,13 @@ int orc_pack_vmeta(int d, int64_t T, const uint16_t* scale, const uint16_t* zero
  * Cache buffers are laid out [B][hkv][cap ...] as in the packing comments above. Tokens past the
  * last whole group (n_ctx % 32 of them) come from the dense tails ktail / vtail [B][hkv][32][d]
  * (row t % 32; f32, or bfloat16 bits when the dtype is 1) with exact keys and values: no base
- * code, no side code. The tails may be NULL when n_ctx is a multiple of 32. */
+ * code, no side code. The tails may be NULL when n_ctx is a multiple of 32. base_bits (2, 3 or 4)
+ * selects the key-code packing: 2-bit words, or one code per nibble for 3 and 4 bits. */
 int orc_decode(int d, int hq, int hkv, int r, int value_mode, int value_dtype, int B, int64_t cap,
                int64_t n_ctx, const uint8_t* kcode, const uint16_t* kmeta, const uint8_t* scode,
                const uint16_t* ssc, const void* vdense, const uint8_t* vcode, const uint16_t* vmeta,
                int key_dtype, const void* ktail, const void* vtail, const float* U, const float* q, double kappa,
-               int b_begin, int b_end, double* logits, double* out);
+               int b_begin, int b_end, double* logits, double* out, int base_bits);
 
 /* Value rows of stream (b, h) as the cache holds them, in fp64: out [n_ctx][d] (dense values as
  * stored, 2-bit values as code * s + z, tokens past the last whole group from vtail). Cache

@@ -53,12 +53,13 @@ def lib():
         L.orc_encode_keys.argtypes = [I, I, I, I, I64, P, P, P, P, P, P, P, P, P]
         L.orc_quantize_values.argtypes = [I, I, I64, P, P, P, P]
         L.orc_pack_kcode.argtypes = [I, I64, P, P]
+        L.orc_pack_kcode4.argtypes = [I, I64, P, P]
         L.orc_pack_kmeta.argtypes = [I, I64, P, P, P]
         L.orc_pack_scode.argtypes = [I, I64, P, P]
         L.orc_pack_vdense.argtypes = [I, I64, I, P, P]
         L.orc_pack_vcode.argtypes = [I, I64, P, P]
         L.orc_pack_vmeta.argtypes = [I, I64, P, P, P]
-        L.orc_decode.argtypes = [I, I, I, I, I, I, I, I64, I64, P, P, P, P, P, P, P, I, P, P, P, P, D, I, I, P, P]
+        L.orc_decode.argtypes = [I, I, I, I, I, I, I, I64, I64, P, P, P, P, P, P, P, I, P, P, P, P, D, I, I, P, P, I]
         L.orc_value_rows.argtypes = [I, I, I, I, I64, I64, P, P, P, P, I, I, P]
         _lib = L
     return _lib
@@ -145,12 +146,13 @@ def quantize_values(v, bits: int = 2):
     return dict(codes=codes, scale=scale, zero=zero)
 
 
-def empty_cache(B, Hkv, cap, d, r, value_mode, value_dtype, key_dtype=None):
+def empty_cache(B, Hkv, cap, d, r, value_mode, value_dtype, key_dtype=None, base_bits=2):
     """Zero-filled buffers of the cache format (numpy, host). With key_dtype given, the dense tails
     of the unfinished last group are included: ktail / vtail [B][Hkv][32][d] in the key / value
-    dtype (f32, or bfloat16 bit patterns)."""
+    dtype (f32, or bfloat16 bit patterns). base_bits 2 packs four key codes per byte; 3 and 4 one
+    code per nibble (kcode rows of d/2 bytes)."""
     c = dict(
-        kcode=np.zeros((B, Hkv, cap, d // 4), np.uint8),
+        kcode=np.zeros((B, Hkv, cap, d // 4 if base_bits == 2 else d // 2), np.uint8),
         kmeta=np.zeros((B, Hkv, cap // GROUP, 2, d), np.uint16),
         scode=np.zeros((B, Hkv, cap, max(r // 2, 0)), np.uint8),
         ssc=np.zeros((B, Hkv, cap), np.uint16),
@@ -223,8 +225,12 @@ def _write_groups(cache, b, h, start, k, v, U_h, value_mode, value_dtype, bits, 
     enc = encode_keys(k, U_h, bits, side_bits)
     L = lib()
     g0, g1 = start // GROUP, (start + n) // GROUP
-    kc = np.zeros((n, d // 4), np.uint8)
-    _check(L.orc_pack_kcode(d, n, _p(enc["codes"]), _p(kc)), "pack_kcode")
+    if bits == 2:
+        kc = np.zeros((n, d // 4), np.uint8)
+        _check(L.orc_pack_kcode(d, n, _p(enc["codes"]), _p(kc)), "pack_kcode")
+    else:
+        kc = np.zeros((n, d // 2), np.uint8)
+        _check(L.orc_pack_kcode4(d, n, _p(enc["codes"]), _p(kc)), "pack_kcode4")
     cache["kcode"][b, h, start:start + n] = kc
     km = np.zeros((n // GROUP, 2, d), np.uint16)
     _check(L.orc_pack_kmeta(d, n, _p(enc["scale"]), _p(enc["zero"]), _p(km)), "pack_kmeta")
@@ -242,7 +248,7 @@ def _write_groups(cache, b, h, start, k, v, U_h, value_mode, value_dtype, bits, 
             _check(L.orc_pack_vdense(d, n, eb, _p(src), _p(dst)), "pack_vdense")
             cache["v"][b, h, g0:g1] = dst
         else:
-            vq = quantize_values(v, bits)
+            vq = quantize_values(v, 2)  # 2-bit values whatever the key base bits
             vc = np.zeros((n // GROUP, d * 8), np.uint8)
             _check(L.orc_pack_vcode(d, n, _p(vq["codes"]), _p(vc)), "pack_vcode")
             cache["vcode"][b, h, g0:g1] = vc
@@ -281,10 +287,12 @@ def decode(cache, q, U, n_ctx, kappa=1.0, value_mode=0, value_dtype=1, b_range=N
     Uc = None if U is None else np.ascontiguousarray(U, dtype=np.float32)
     kt = arrs.get("ktail")
     key_dtype = 0 if kt is None or kt.dtype == np.float32 else 1
+    layout_bits = 2 if kcode.shape[3] * 4 == d else 4  # packing only: the levels do not enter k_hat
     _check(lib().orc_decode(d, Hq, Hkv, r, value_mode, value_dtype, B, cap, n_ctx, _p(arrs["kcode"]),
                             _p(arrs["kmeta"]), _p(arrs["scode"]) if r else None, _p(arrs["ssc"]) if r else None,
                             _p(arrs.get("v")), _p(arrs.get("vcode")), _p(arrs.get("vmeta")), key_dtype, _p(kt),
-                            _p(arrs.get("vtail")), _p(Uc), _p(q), float(kappa), b0, b1, _p(logits), _p(out)),
+                            _p(arrs.get("vtail")), _p(Uc), _p(q), float(kappa), b0, b1, _p(logits), _p(out),
+                            layout_bits),
            "decode")
     return logits, out
 

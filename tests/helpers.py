@@ -26,7 +26,8 @@ def oracle_cache(w: synth.Workload, U: np.ndarray | None, batch: int | None = No
     T = w.n_ctx if n_tok is None else n_tok
     cap = T if cap is None else cap
     r = 0 if U is None else U.shape[2]
-    cache = orc.empty_cache(B, w.n_kv_heads, cap, w.head_dim, r, VMODE[w.value_mode], VDT[w.value_dtype])
+    cache = orc.empty_cache(B, w.n_kv_heads, cap, w.head_dim, r, VMODE[w.value_mode], VDT[w.value_dtype],
+                            base_bits=w.base_bits if bits is None else bits)
     encs = {}
     for b in range(B):
         for h in range(w.n_kv_heads):
