@@ -35,7 +35,10 @@
  *   kcode  u8   [B][Hkv][cap][d/4]       2-bit base codes, d/16 little-endian 32-bit words per
  *                                        token: channel 16m + j (j = 8q + 2b + e) at bit
  *                                        8b + 4e + 2q of word m (one mask or one shift leaves
- *                                        one code per nibble, in channel order)
+ *                                        one code per nibble, in channel order).
+ *                                        base_bits 3 or 4: [B][Hkv][cap][d/2], one code per
+ *                                        nibble, d/8 words per token, channel 8m + j at bit
+ *                                        4*(j/2) + 16*(j%2) of word m
  *   kmeta  fp16 [B][Hkv][cap/G][2][d]    per (group, channel): row 0 = step s, row 1 = zero z
  *   scode  u8   [B][Hkv][cap][r/2]       4-bit side codes u = zc + 8; component 2i in the low
  *                                        nibble of byte i, component 2i+1 in the high nibble
@@ -93,7 +96,8 @@ typedef struct headq_config {
                           query head hq reads KV head hq / g */
   int32_t batch;       /* B >= 1 */
   int64_t capacity;    /* tokens per (b, h) stream, a positive multiple of 32 */
-  int32_t base_bits;   /* bits of the base key code: 2 */
+  int32_t base_bits;   /* bits of the base key code: 2 (four codes per byte), or 3 / 4 (one code per
+                          nibble, 7 / 15 levels; values stay 2-bit) */
   int32_t group;       /* tokens per base-quantizer group: 32 */
   int32_t rank;        /* r: 0, 4, 8, 16 or 32 (0 = base quantizer only) */
   int32_t side_bits;   /* bits per side-code component: 4 */
@@ -264,7 +268,7 @@ const char* headq_status_string(headq_status s);
 
 /* ---- layout sizes in bytes (inline helpers, not exported) ---- */
 static inline size_t headq_kcode_bytes(const headq_config* c) {
-  return (size_t)c->batch * c->n_kv_heads * c->capacity * (c->head_dim / 4);
+  return (size_t)c->batch * c->n_kv_heads * c->capacity * (c->base_bits == 2 ? c->head_dim / 4 : c->head_dim / 2);
 }
 static inline size_t headq_kmeta_bytes(const headq_config* c) {
   return (size_t)c->batch * c->n_kv_heads * (c->capacity / 32) * 2 * c->head_dim * 2;
@@ -285,7 +289,9 @@ static inline size_t headq_vmeta_bytes(const headq_config* c) {
   return (size_t)c->batch * c->n_kv_heads * c->capacity * (c->head_dim / 32) * 2 * 2;
 }
 /* Paged pools: bytes of one page (one 32-token group of every KV head) of each array. */
-static inline size_t headq_page_kcode_bytes(const headq_config* c) { return (size_t)c->n_kv_heads * 32 * (c->head_dim / 4); }
+static inline size_t headq_page_kcode_bytes(const headq_config* c) {
+  return (size_t)c->n_kv_heads * 32 * (c->base_bits == 2 ? c->head_dim / 4 : c->head_dim / 2);
+}
 static inline size_t headq_page_kmeta_bytes(const headq_config* c) { return (size_t)c->n_kv_heads * 2 * c->head_dim * 2; }
 static inline size_t headq_page_scode_bytes(const headq_config* c) { return (size_t)c->n_kv_heads * 32 * (c->rank / 2); }
 static inline size_t headq_page_ssc_bytes(const headq_config* c) { return (size_t)c->n_kv_heads * 32 * 2; }

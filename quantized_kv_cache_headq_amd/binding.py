@@ -225,7 +225,7 @@ class DeviceCache:
         self.cfg = cfg
         B, H, cap, d, r = cfg.batch, cfg.n_kv_heads, cfg.capacity, cfg.head_dim, cfg.rank
         u8, i16 = torch.uint8, torch.int16
-        self.kcode = torch.zeros((B, H, cap, d // 4), dtype=u8, device=device)
+        self.kcode = torch.zeros((B, H, cap, d // 4 if cfg.base_bits == 2 else d // 2), dtype=u8, device=device)
         self.kmeta = torch.zeros((B, H, cap // GROUP, 2, d), dtype=i16, device=device)
         self.scode = torch.zeros((B, H, cap, max(r // 2, 1)), dtype=u8, device=device) if r else None
         self.ssc = torch.zeros((B, H, cap), dtype=i16, device=device) if r else None
@@ -308,7 +308,7 @@ class PagedDeviceCache(DeviceCache):
         self.n_pages, self.max_pages = n_pages, max_pages
         H, d, r, P = cfg.n_kv_heads, cfg.head_dim, cfg.rank, n_pages
         u8, i16 = torch.uint8, torch.int16
-        self.kcode = torch.zeros((P, H, GROUP, d // 4), dtype=u8, device=device)
+        self.kcode = torch.zeros((P, H, GROUP, d // 4 if cfg.base_bits == 2 else d // 2), dtype=u8, device=device)
         self.kmeta = torch.zeros((P, H, 2, d), dtype=i16, device=device)
         self.scode = torch.zeros((P, H, GROUP, max(r // 2, 1)), dtype=u8, device=device) if r else None
         self.ssc = torch.zeros((P, H, GROUP), dtype=i16, device=device) if r else None

@@ -53,10 +53,10 @@ __device__ __forceinline__ void minmax_step_zero(float lo, float hi, float level
   inv = (s == 0.0f) ? 0.0f : 1.0f / s;
 }
 
-__device__ __forceinline__ uint32_t base_code(float k, float z, float inv) {
+__device__ __forceinline__ uint32_t base_code(float k, float z, float inv, float levels) {
   float c = __builtin_rintf((k - z) * inv);
   c = c < 0.0f ? 0.0f : c;
-  c = c > 3.0f ? 3.0f : c;
+  c = c > levels ? levels : c;
   return (uint32_t)c;
 }
 
@@ -173,6 +173,7 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
   __shared__ float U_s[UL && R > 0 ? D * R : 1];
 
   const int h = blockIdx.y, b = blockIdx.z;
+  const float klev = (float)a.key_levels;  // base-code levels of the keys (values are 2-bit: 3)
   // this row's append position; a row that would pass the capacity is left untouched
   const int64_t st = a.row_start ? (int64_t)a.row_start[b] : a.start;
   if (st < 0 || st + a.n_new > a.cap) return;
@@ -224,7 +225,7 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
     }
     float s, z, inv;
     uint16_t sb, zb;
-    minmax_step_zero(lo, hi, 3.0f, s, z, inv, sb, zb);
+    minmax_step_zero(lo, hi, klev, s, z, inv, sb, zb);
     if (tl.whole(gl)) {
       uint16_t* meta = a.kmeta + a.map.block(b, h, tl.group(gl)) * 2 * D;
       meta[c] = sb;
@@ -236,21 +237,27 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
   }
   __syncthreads();
 
-  // 3. codes (16 channels -> one 32-bit word) and residuals e = k - fma(code, s, z)
+  // 3. codes (16 channels -> one 32-bit word at 2 bits, two nibble words at 3 or 4 bits) and
+  // residuals e = k - fma(code, s, z)
+  const bool nib = a.key_levels != 3;
   for (int i = tid; i < kRows * (D / 16); i += kThreads) {
     const int row = i / (D / 16), c0 = (i % (D / 16)) * 16, gl = row / kGroup;
-    uint32_t word = 0;
+    uint32_t word = 0, w4[2] = {0u, 0u};
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int c = c0 + j, m = gl * D + c;
       const float k = ke[row][c];
-      const uint32_t code = base_code(k, z_s[m], inv_s[m]);
+      const uint32_t code = base_code(k, z_s[m], inv_s[m], klev);
       word |= code << kcode_bit(j);
+      w4[j / 8] |= code << kcode4_bit(j % 8);
       ke[row][c] = k - __builtin_fmaf((float)code, s_s[m], z_s[m]);
     }
     if (tl.whole(gl)) {
       const int64_t tok = row_token(tl, row);
-      *reinterpret_cast<uint32_t*>(a.kcode + a.map.row(b, h, tok) * (D / 4) + c0 / 4) = word;
+      if (nib)
+        *reinterpret_cast<uint2*>(a.kcode + a.map.row(b, h, tok) * (D / 2) + c0 / 2) = make_uint2(w4[0], w4[1]);
+      else
+        *reinterpret_cast<uint32_t*>(a.kcode + a.map.row(b, h, tok) * (D / 4) + c0 / 4) = word;
     }
   }
 
@@ -419,7 +426,7 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const int row = gl * kGroup + t0 + 4 * q + e;
-          v |= base_code(ke[row][c], z_s[row * NG + gc], inv_s[row * NG + gc]) << (4 * e + 2 * q);
+          v |= base_code(ke[row][c], z_s[row * NG + gc], inv_s[row * NG + gc], 3.0f) << (4 * e + 2 * q);
         }
       if (tl.whole(gl)) a.vcode[a.map.block(b, h, tl.group(gl)) * D * 8 + byte] = (uint8_t)v;
     }

@@ -126,10 +126,11 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
       const int t = tid / 8, sub = tid % 8;
       const int64_t tok = gi * kGroup + t;
       const int64_t trow = a.map.row(b, h, tok);
-      const uint32_t* kc = (const uint32_t*)(a.kcode + trow * (D / 4));
-      uint32_t words[D / 16];
+      const bool nib = a.key_nib;  // 3- or 4-bit codes, one per nibble (rows of d/2 bytes)
+      const uint32_t* kc = (const uint32_t*)(a.kcode + trow * (nib ? D / 2 : D / 4));
+      uint32_t words[D / 8];
 #pragma unroll
-      for (int w = 0; w < D / 16; ++w) words[w] = kc[w];
+      for (int w = 0; w < D / 8; ++w) words[w] = (nib || w < D / 16) ? kc[w] : 0u;
       float sg = 0.0f;
       uint32_t sw[RU / 8 > 0 ? RU / 8 : 1];
       if constexpr (R > 0) {
@@ -144,10 +145,18 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a) {
       }
       for (int hh = sub; hh < g; hh += 8) {
         float acc = 0.0f;
+        if (nib) {
 #pragma unroll
-        for (int c = 0; c < D; ++c) {
-          const float code = (float)((words[c / 16] >> kcode_bit(c % 16)) & 3u);
-          acc = fmaf(qbar[hh][c], fmaf(code, sz[0][c], sz[1][c]), acc);
+          for (int c = 0; c < D; ++c) {
+            const float code = (float)((words[c / 8] >> kcode4_bit(c % 8)) & 15u);
+            acc = fmaf(qbar[hh][c], fmaf(code, sz[0][c], sz[1][c]), acc);
+          }
+        } else {
+#pragma unroll
+          for (int c = 0; c < D; ++c) {
+            const float code = (float)((words[c / 16] >> kcode_bit(c % 16)) & 3u);
+            acc = fmaf(qbar[hh][c], fmaf(code, sz[0][c], sz[1][c]), acc);
+          }
         }
         if constexpr (R > 0) {
           float cs = 0.0f;

@@ -90,9 +90,10 @@ struct Stream {
 // Every array of a group is contiguous in the cache, so each is fetched with one load
 // instruction in which lane L takes bytes [L*w, L*w + w) (w = 16, 8, 4, 2 or 1): fully
 // coalesced, whatever pieces the matrix operands need afterwards.
-template <int D, int R, bool VQ2>
+template <int D, int R, bool VQ2, bool NB>
 struct KSide {
-  static constexpr int KC = kGroup * D / 4, KM = 4 * D, SC = kGroup * R / 2, SG = R > 0 ? kGroup * 2 : 0;
+  // key codes: 2 bits (4 per byte) or one per nibble (3- and 4-bit base codes, NB)
+  static constexpr int KC = kGroup * D / (NB ? 2 : 4), KM = 4 * D, SC = kGroup * R / 2, SG = R > 0 ? kGroup * 2 : 0;
   static constexpr int VM = VQ2 ? 4 * D : 0;
   static constexpr int OFF_KM = KC, OFF_SC = KC + KM, OFF_SG = KC + KM + SC, OFF_VM = KC + KM + SC + SG;
   static constexpr int BYTES = (KC + KM + SC + SG + VM + 15) / 16 * 16;
@@ -100,6 +101,7 @@ struct KSide {
 
 template <int N>
 struct Bytes;  // N bytes held by one lane
+template <> struct Bytes<32> { using T = u32x8; };
 template <> struct Bytes<16> { using T = u32x4; };
 template <> struct Bytes<8> { using T = u32x2; };
 template <> struct Bytes<4> { using T = uint32_t; };
@@ -108,6 +110,11 @@ template <> struct Bytes<1> { using T = uint8_t; };
 
 template <int N>
 __device__ __forceinline__ typename Bytes<N>::T load_piece(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  if constexpr (N == 32) {
+    const u32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kStream);
+    const u32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16, soff, kStream);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
   if constexpr (N == 16) return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kStream);
   if constexpr (N == 8) return __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kStream);
   if constexpr (N == 4) return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kStream);
@@ -123,10 +130,10 @@ __device__ __forceinline__ uint32_t word_of(const typename Bytes<N>::T& x, int w
 }
 
 // Raw bytes of one 32-token group as one lane holds them (filled one group ahead).
-template <int D, int R, bool VQ2>
+template <int D, int R, bool VQ2, bool NB>
 struct GroupRaw {
   static constexpr int NCT = D / 16;            // channel tiles of the P.V product
-  typename Bytes<D / 8>::T kc;                  // lane's share of the packed key codes
+  typename Bytes<KSide<D, R, VQ2, NB>::KC / 64>::T kc;  // lane's share of the packed key codes
   typename Bytes<D / 16>::T km;                 // lane's share of the key step/zero rows
   typename Bytes<(R > 0 ? R / 4 : 1)>::T sc;    // lane's share of the side codes
   uint8_t sg;                                   // lane's share of the sigmas
@@ -135,10 +142,10 @@ struct GroupRaw {
   typename Bytes<D / 16>::T vm;                 // 2-bit: lane's share of the value step/zero rows
 };
 
-template <int D, int R, bool VQ2>
-__device__ __forceinline__ void load_group(GroupRaw<D, R, VQ2>& g, const Stream& s_stream, const DecodeArgs& a, int h,
+template <int D, int R, bool VQ2, bool NB>
+__device__ __forceinline__ void load_group(GroupRaw<D, R, VQ2, NB>& g, const Stream& s_stream, const DecodeArgs& a, int h,
                                            int page_v, int lane, int n, int quad, int gi_in) {
-  using KS = KSide<D, R, VQ2>;
+  using KS = KSide<D, R, VQ2, NB>;
   // the group index is wave-uniform; saying so keeps every group offset in a scalar register
   // (a per-lane offset would make the compiler loop over the lanes around each buffer load)
   int gi = __builtin_amdgcn_readfirstlane(gi_in);
@@ -164,7 +171,7 @@ __device__ __forceinline__ void load_group(GroupRaw<D, R, VQ2>& g, const Stream&
     }
     gi = 0;
   }
-  g.kc = load_piece<D / 8>(s.kcode, lane * (D / 8), gi * KS::KC);
+  g.kc = load_piece<KS::KC / 64>(s.kcode, lane * (KS::KC / 64), gi * KS::KC);
   g.km = load_piece<D / 16>(s.kmeta, lane * (D / 16), gi * KS::KM);
   if constexpr (R > 0) {
     g.sc = load_piece<R / 4>(s.scode, lane * (R / 4), gi * KS::SC);
@@ -205,17 +212,17 @@ struct Fixed {
 };
 
 // One 32-token group: scores, online-softmax update, P.V accumulation.
-template <int D, int R, bool VQ2>
-__device__ __forceinline__ void process_group(const GroupRaw<D, R, VQ2>& cur, const Fixed<D, R>& f, uint8_t* slot,
+template <int D, int R, bool VQ2, bool NB>
+__device__ __forceinline__ void process_group(const GroupRaw<D, R, VQ2, NB>& cur, const Fixed<D, R>& f, uint8_t* slot,
                                               const DecodeArgs& a, int gi, int b, int hq0, int g, int lane, int n,
                                               int quad, floatx4* o_acc, float* z_acc, float& m_run, float& l_run) {
   constexpr int NKT = D / 32, NCT = D / 16, NG = D / 32;
-  using KS = KSide<D, R, VQ2>;
+  using KS = KSide<D, R, VQ2, NB>;
   // Staged bytes through the wave's LDS slot. Lanes read what other lanes wrote, so the accesses
   // are ordered by wave-scope fences (the wave executes its LDS operations in order; the fences
   // stop the compiler from moving reads across the writes, in either direction).
   lds_wave_fence();
-  *reinterpret_cast<typename Bytes<D / 8>::T*>(slot + lane * (D / 8)) = cur.kc;
+  *reinterpret_cast<typename Bytes<KS::KC / 64>::T*>(slot + lane * (KS::KC / 64)) = cur.kc;
   *reinterpret_cast<typename Bytes<D / 16>::T*>(slot + KS::OFF_KM + lane * (D / 16)) = cur.km;
   if constexpr (R > 0) {
     *reinterpret_cast<typename Bytes<R / 4>::T*>(slot + KS::OFF_SC + lane * (R / 4)) = cur.sc;
@@ -225,17 +232,15 @@ __device__ __forceinline__ void process_group(const GroupRaw<D, R, VQ2>& cur, co
   lds_wave_fence();
   const _Float16* km_h = reinterpret_cast<const _Float16*>(slot + KS::OFF_KM);
   const int row_tok0 = 8 * (n / 4) + (n % 4);  // token of this lane's row in tile 0 (tile 1: +4)
-  uint32_t kcw[2][D / 64];                      // packed codes of the row tokens, this lane's piece
+  // packed codes of the row tokens, this lane's piece (channels (d/4)*quad .. +d/4): d/64 words
+  // of 2-bit codes, or d/32 nibble words
+  constexpr int KW = NB ? D / 32 : D / 64;
+  uint32_t kcw[2][KW];
 #pragma unroll
   for (int T = 0; T < 2; ++T) {
-    const uint8_t* p = slot + (row_tok0 + 4 * T) * (D / 4) + (D / 16) * quad;
-    if constexpr (D == 128) {
-      const u32x2 w = *reinterpret_cast<const u32x2*>(p);
-      kcw[T][0] = w[0];
-      kcw[T][1] = w[1];
-    } else {
-      kcw[T][0] = *reinterpret_cast<const uint32_t*>(p);
-    }
+    const uint8_t* p = slot + (row_tok0 + 4 * T) * (KS::KC / 32) + 4 * KW * quad;
+#pragma unroll
+    for (int w = 0; w < KW; ++w) kcw[T][w] = reinterpret_cast<const uint32_t*>(p)[w];
   }
 
   // zero term q.z (identical for every token row), then codes . (q o s) on top of it
@@ -260,8 +265,13 @@ __device__ __forceinline__ void process_group(const GroupRaw<D, R, VQ2>& cur, co
     for (int T = 0; T < 2; ++T) {
       // k-tile t covers channels (d/4)*quad + 8t .. +7: the even (t even) or odd (t odd) run of
       // the lane's word t/2
-      const uint32_t w = kcw[T][(D == 128) ? (t >> 1) : 0];
-      const half8_t ac = key_codes8((t & 1) ? odd_codes(w) : even_codes(w));
+      half8_t ac;
+      if constexpr (NB) {
+        ac = key_codes8_nib(kcw[T][t]);  // nibble word t: channels (d/4)*quad + 8t .. +7
+      } else {
+        const uint32_t w = kcw[T][(D == 128) ? (t >> 1) : 0];
+        ac = key_codes8((t & 1) ? odd_codes(w) : even_codes(w));
+      }
       acc[T] = mfma_f16(ac, p_hi, acc[T]);
       acc[T] = mfma_f16(ac, p_lo, acc[T]);
     }
@@ -489,14 +499,14 @@ __device__ __forceinline__ void process_tail(const DecodeArgs& a, int64_t n_ctx,
   }
 }
 
-template <int D, int R, bool VQ2>
+template <int D, int R, bool VQ2, bool NB>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int NKT = D / 32, NCT = D / 16, NG = D / 32;
   constexpr int RU = R > 0 ? R : 1;
   __shared__ float qs[kMaxGqa][D];            // scaled queries
   __shared__ float qu_s[kMaxGqa][RU];         // U^T q (scaled)
   __shared__ float inv_scale_s[kMaxGqa];      // 2^e undoing the per-head query scale
-  __shared__ u32x4 kslot[kWaves][KSide<D, R, VQ2>::BYTES / 16];  // per-wave staging of a group
+  __shared__ u32x4 kslot[kWaves][KSide<D, R, VQ2, NB>::BYTES / 16];  // per-wave staging of a group
   __shared__ float m_w[kWaves][kMaxGqa], l_w[kWaves][kMaxGqa];
   __shared__ float o_w[kWaves][kMaxGqa][D];
 
@@ -534,7 +544,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // prologue so that their latency overlaps it.
   Stream s;
   const int groups_cap = (int)(a.cap / kGroup);
-  s.kcode = make_rsrc(a.kcode + bh * a.cap * (D / 4), a.cap * (D / 4));
+  constexpr int KROW = KSide<D, R, VQ2, NB>::KC / kGroup;  // key-code bytes per token
+  s.kcode = make_rsrc(a.kcode + bh * a.cap * KROW, a.cap * KROW);
   s.kmeta = make_rsrc(a.kmeta + bh * groups_cap * 2 * D, (int64_t)groups_cap * 4 * D);
   s.scode = make_rsrc(R > 0 ? a.scode + bh * a.cap * (R / 2) : a.kcode, R > 0 ? a.cap * (R / 2) : 0);
   s.ssc = make_rsrc(R > 0 ? a.ssc + bh * a.cap : a.kmeta, R > 0 ? a.cap * 2 : 0);
@@ -562,11 +573,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
                 a.map.block_table ? a.map.max_pages * 4 : 0);
   auto page_at = [&](int j) { return j < n_groups ? request_page(a, table_row, group_at(j)) : 0; };
   int pa = 0, pb = 0;          // pages of the next groups loaded into ga / gb (paged caches)
-  GroupRaw<D, R, VQ2> ga, gb;  // ping-pong register sets: one group computed while the next loads
+  GroupRaw<D, R, VQ2, NB> ga, gb;  // ping-pong register sets: one group computed while the next loads
   auto first_loads = [&]() {
-    if (j_begin < n_groups) load_group<D, R, VQ2>(ga, s, a, h, page_at(j_begin), lane, n, quad, group_at(j_begin));
+    if (j_begin < n_groups) load_group<D, R, VQ2, NB>(ga, s, a, h, page_at(j_begin), lane, n, quad, group_at(j_begin));
     if (j_begin + W < n_groups)
-      load_group<D, R, VQ2>(gb, s, a, h, page_at(j_begin + W), lane, n, quad, group_at(j_begin + W));
+      load_group<D, R, VQ2, NB>(gb, s, a, h, page_at(j_begin + W), lane, n, quad, group_at(j_begin + W));
     pa = page_at(j_begin + 2 * W);
     pb = page_at(j_begin + 3 * W);
   };
@@ -645,16 +656,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // ---- this wave's groups
   uint8_t* slot = reinterpret_cast<uint8_t*>(kslot[wave]);
   for (int j = j_begin; j < n_groups; j += 2 * W) {
-    process_group<D, R, VQ2>(ga, f, slot, a, group_at(j), b, hq0, g, lane, n, quad, o_acc, z_acc, m_run, l_run);
+    process_group<D, R, VQ2, NB>(ga, f, slot, a, group_at(j), b, hq0, g, lane, n, quad, o_acc, z_acc, m_run, l_run);
     if (j + W >= n_groups) break;
     if (j + 2 * W < n_groups) {
-      load_group<D, R, VQ2>(ga, s, a, h, pa, lane, n, quad, group_at(j + 2 * W));
+      load_group<D, R, VQ2, NB>(ga, s, a, h, pa, lane, n, quad, group_at(j + 2 * W));
       pa = page_at(j + 4 * W);
     }
-    process_group<D, R, VQ2>(gb, f, slot, a, group_at(j + W), b, hq0, g, lane, n, quad, o_acc, z_acc, m_run,
+    process_group<D, R, VQ2, NB>(gb, f, slot, a, group_at(j + W), b, hq0, g, lane, n, quad, o_acc, z_acc, m_run,
                              l_run);
     if (j + 3 * W < n_groups) {
-      load_group<D, R, VQ2>(gb, s, a, h, pb, lane, n, quad, group_at(j + 3 * W));
+      load_group<D, R, VQ2, NB>(gb, s, a, h, pb, lane, n, quad, group_at(j + 3 * W));
       pb = page_at(j + 5 * W);
     }
   }
@@ -763,15 +774,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   if (tid == 0) atomicExch(a.ws_count + bh, 0u);
 }
 
-template <int D, bool VQ2>
+template <int D, bool VQ2, bool NB>
 hipError_t launch_r(const DecodeArgs& a, hipStream_t s) {
   dim3 grid((unsigned)a.n_splits, (unsigned)a.hkv, (unsigned)a.batch);
   switch (a.r) {
-    case 0: hipLaunchKernelGGL((decode_mfma_kernel<D, 0, VQ2>), grid, dim3(kThreads), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((decode_mfma_kernel<D, 4, VQ2>), grid, dim3(kThreads), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((decode_mfma_kernel<D, 8, VQ2>), grid, dim3(kThreads), 0, s, a); break;
-    case 16: hipLaunchKernelGGL((decode_mfma_kernel<D, 16, VQ2>), grid, dim3(kThreads), 0, s, a); break;
-    case 32: hipLaunchKernelGGL((decode_mfma_kernel<D, 32, VQ2>), grid, dim3(kThreads), 0, s, a); break;
+    case 0: hipLaunchKernelGGL((decode_mfma_kernel<D, 0, VQ2, NB>), grid, dim3(kThreads), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((decode_mfma_kernel<D, 4, VQ2, NB>), grid, dim3(kThreads), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((decode_mfma_kernel<D, 8, VQ2, NB>), grid, dim3(kThreads), 0, s, a); break;
+    case 16: hipLaunchKernelGGL((decode_mfma_kernel<D, 16, VQ2, NB>), grid, dim3(kThreads), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((decode_mfma_kernel<D, 32, VQ2, NB>), grid, dim3(kThreads), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -781,8 +792,13 @@ hipError_t launch_r(const DecodeArgs& a, hipStream_t s) {
 
 hipError_t launch_decode_mfma_split(const DecodeArgs& a, hipStream_t s) {
   const bool q2 = a.value_mode == HEADQ_V_Q2;
-  if (a.d == 64) return q2 ? launch_r<64, true>(a, s) : launch_r<64, false>(a, s);
-  if (a.d == 128) return q2 ? launch_r<128, true>(a, s) : launch_r<128, false>(a, s);
+  if (a.key_nib) {
+    if (a.d == 64) return q2 ? launch_r<64, true, true>(a, s) : launch_r<64, false, true>(a, s);
+    if (a.d == 128) return q2 ? launch_r<128, true, true>(a, s) : launch_r<128, false, true>(a, s);
+  } else {
+    if (a.d == 64) return q2 ? launch_r<64, true, false>(a, s) : launch_r<64, false, false>(a, s);
+    if (a.d == 128) return q2 ? launch_r<128, true, false>(a, s) : launch_r<128, false, false>(a, s);
+  }
   return hipErrorInvalidValue;
 }
 

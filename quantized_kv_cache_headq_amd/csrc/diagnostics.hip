@@ -240,7 +240,7 @@ __device__ __forceinline__ double raw_elem(const uint32_t* w, int c) {
 }
 
 // ---- stream pass
-template <int D, int R, bool KBF>
+template <int D, int R, bool KBF, bool NB>
 __global__ __launch_bounds__(kThreads) void diag_stream_kernel(DiagArgs a) {
   constexpr int RU = R > 0 ? R : 1;
   constexpr int KW = KBF ? 16 : 32;  // 32-bit words of 32 reference-key channels
@@ -302,13 +302,21 @@ __global__ __launch_bounds__(kThreads) void diag_stream_kernel(DiagArgs a) {
               const uint4 v = reinterpret_cast<const uint4*>(meta + D + 32 * blk)[i];
               zw[4 * i] = v.x, zw[4 * i + 1] = v.y, zw[4 * i + 2] = v.z, zw[4 * i + 3] = v.w;
             }
-            const uint2 cw = *reinterpret_cast<const uint2*>(a.kcode + row * (D / 4) + 8 * blk);
+            // the block's packed codes: 2 words of 2-bit codes, or 4 nibble words
+            uint32_t cw[NB ? 4 : 2];
+            if constexpr (NB) {
+              const uint4 u = *reinterpret_cast<const uint4*>(a.kcode + row * (D / 2) + 16 * blk);
+              cw[0] = u.x, cw[1] = u.y, cw[2] = u.z, cw[3] = u.w;
+            } else {
+              const uint2 u = *reinterpret_cast<const uint2*>(a.kcode + row * (D / 4) + 8 * blk);
+              cw[0] = u.x, cw[1] = u.y;
+            }
 #pragma unroll
             for (int cc = 0; cc < 32; ++cc) {
               // keep the scheduler from converting all 32 channels at once (register pressure)
               if (cc % 8 == 0) __builtin_amdgcn_sched_barrier(0);
-              const uint32_t word = cc < 16 ? cw.x : cw.y;
-              const double code = (double)((word >> kcode_bit(cc % 16)) & 3u);
+              const double code = NB ? (double)((cw[cc / 8] >> kcode4_bit(cc % 8)) & 15u)
+                                     : (double)((cw[cc / 16] >> kcode_bit(cc % 16)) & 3u);
               const double sv = f16_bits(cc % 2 ? sw[cc / 2] >> 16 : sw[cc / 2] & 0xffffu);
               const double zv = f16_bits(cc % 2 ? zw[cc / 2] >> 16 : zw[cc / 2] & 0xffffu);
               const double kk = raw_elem<KBF>(kw, cc);
@@ -458,15 +466,15 @@ __global__ __launch_bounds__(64) void diag_merge_kernel(DiagArgs a) {
   o[HEADQ_DIAG_ENTROPY] = log(S[0]) + Mx - S[5] / S[0];
 }
 
-template <int D, bool KBF>
+template <int D, bool KBF, bool NB>
 hipError_t launch_dk(const DiagArgs& a, hipStream_t s) {
   dim3 grid((unsigned)a.n_splits, (unsigned)a.hkv, (unsigned)a.batch);
   switch (a.r) {
-    case 0: hipLaunchKernelGGL((diag_stream_kernel<D, 0, KBF>), grid, dim3(kThreads), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((diag_stream_kernel<D, 4, KBF>), grid, dim3(kThreads), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((diag_stream_kernel<D, 8, KBF>), grid, dim3(kThreads), 0, s, a); break;
-    case 16: hipLaunchKernelGGL((diag_stream_kernel<D, 16, KBF>), grid, dim3(kThreads), 0, s, a); break;
-    case 32: hipLaunchKernelGGL((diag_stream_kernel<D, 32, KBF>), grid, dim3(kThreads), 0, s, a); break;
+    case 0: hipLaunchKernelGGL((diag_stream_kernel<D, 0, KBF, NB>), grid, dim3(kThreads), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((diag_stream_kernel<D, 4, KBF, NB>), grid, dim3(kThreads), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((diag_stream_kernel<D, 8, KBF, NB>), grid, dim3(kThreads), 0, s, a); break;
+    case 16: hipLaunchKernelGGL((diag_stream_kernel<D, 16, KBF, NB>), grid, dim3(kThreads), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((diag_stream_kernel<D, 32, KBF, NB>), grid, dim3(kThreads), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -483,7 +491,8 @@ hipError_t launch_d(const DiagArgs& a, hipStream_t s) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  return a.key_bf16 ? launch_dk<D, true>(a, s) : launch_dk<D, false>(a, s);
+  if (a.key_nib) return a.key_bf16 ? launch_dk<D, true, true>(a, s) : launch_dk<D, false, true>(a, s);
+  return a.key_bf16 ? launch_dk<D, true, false>(a, s) : launch_dk<D, false, false>(a, s);
 }
 
 }  // namespace

@@ -38,7 +38,8 @@ headq_status check_config(const headq_config* c) {
   if (c->n_q_heads % c->n_kv_heads) return HEADQ_ERR_SHAPE;
   if (c->n_q_heads / c->n_kv_heads > headq::kMaxGqa) return HEADQ_ERR_UNSUPPORTED;
   if (c->capacity % headq::kGroup) return HEADQ_ERR_ALIGN;
-  if (c->base_bits != 2 || c->group != headq::kGroup || c->side_bits != 4) return HEADQ_ERR_UNSUPPORTED;
+  if (c->base_bits < 2 || c->base_bits > 4 || c->group != headq::kGroup || c->side_bits != 4)
+    return HEADQ_ERR_UNSUPPORTED;
   if (c->rank != 0 && c->rank != 4 && c->rank != 8 && c->rank != 16 && c->rank != 32) return HEADQ_ERR_UNSUPPORTED;
   if ((c->key_dtype != HEADQ_F32 && c->key_dtype != HEADQ_BF16) ||
       (c->value_dtype != HEADQ_F32 && c->value_dtype != HEADQ_BF16) ||
@@ -124,6 +125,7 @@ extern "C" headq_status headq_cache_append(const headq_config* cfg, const headq_
 
   headq::AppendArgs a{};
   a.d = cfg->head_dim;
+  a.key_levels = (1 << cfg->base_bits) - 1;
   a.r = cfg->rank;
   a.hkv = cfg->n_kv_heads;
   a.batch = cfg->batch;
@@ -223,6 +225,7 @@ extern "C" headq_status headq_decode_attn(const headq_config* cfg, const headq_c
 
   headq::DecodeArgs a{};
   a.d = cfg->head_dim;
+  a.key_nib = cfg->base_bits != 2;
   a.r = cfg->rank;
   a.hq = cfg->n_q_heads;
   a.hkv = cfg->n_kv_heads;
@@ -306,6 +309,7 @@ extern "C" headq_status headq_score_diagnostics(const headq_config* cfg, const h
 
   headq::DiagArgs a{};
   a.d = cfg->head_dim;
+  a.key_nib = cfg->base_bits != 2;
   a.r = cfg->rank;
   a.hq = cfg->n_q_heads;
   a.hkv = cfg->n_kv_heads;
@@ -369,6 +373,7 @@ extern "C" headq_status headq_prefill_attn(const headq_config* cfg, const headq_
 
   headq::PrefillArgs a{};
   a.d = cfg->head_dim;
+  a.key_nib = cfg->base_bits != 2;
   a.r = cfg->rank;
   a.hq = cfg->n_q_heads;
   a.hkv = cfg->n_kv_heads;

@@ -21,6 +21,11 @@ constexpr int kMaxSplitsMfma = 128;  // splits per stream of the matrix-core dec
 //   values per 32-token group, lane l = 16*(t/8) + c%16 owns d/8 bytes, two per 16-channel tile
 //          c/16; token item i = t%8 = 4q + 2b + e sits in byte b of that pair at bit 4e + 2q
 __host__ __device__ constexpr int kcode_bit(int j) { return 8 * ((j % 8) / 2) + 4 * (j % 2) + 2 * (j / 8); }
+// 3- and 4-bit base codes, one per nibble: a token row is d/2 bytes, channel 8m + j at bit
+// 4*(j/2) + 16*(j%2) of word m (channels 2i and 2i+1 share nibble i of the two 16-bit halves, which
+// the matrix-core kernels turn into an f16 pair with one mask and one or)
+__host__ __device__ constexpr int kcode4_bit(int j) { return 4 * (j / 2) + 16 * (j % 2); }
+__host__ __device__ constexpr int kcode_row_bytes(int d, bool nib) { return nib ? d / 2 : d / 4; }
 __host__ __device__ constexpr int vcode_pair_offset(int d, int c, int t) {  // byte offset of the 16-bit pair
   return ((16 * ((t % 32) / 8) + c % 16) * (d / 16) + c / 16) * 2;
 }
@@ -57,6 +62,7 @@ struct AppendArgs {
   int64_t cap;                 // tokens per stream in the cache
   int64_t start, n_new;        // token range written (multiples of 32)
   int key_bf16, value_bf16, value_mode;
+  int key_levels;              // base-code levels 2^bits - 1 (3, 7 or 15)
   const void* k;
   int64_t ks_b, ks_h, ks_t;    // key element strides
   const void* v;               // may be null: values untouched
@@ -83,6 +89,7 @@ struct DecodeArgs {
   int chunks_per_split;        // 1 (VALU kernel) or 4 (MFMA kernel: one chunk per wave)
   int use_mfma;                // matrix-core kernel (dense bf16 or 2-bit values)
   int query_bf16, value_bf16, value_mode, out_bf16;
+  int key_nib;                 // 3- or 4-bit base codes (one per nibble)
   float corr_scale;
   const void* q;
   const uint8_t* kcode;
@@ -110,6 +117,7 @@ struct DiagArgs {
   int64_t cap, n_ctx;
   int n_splits;                // workgroups per (b, h); 4 waves each, 64-token chunks per wave
   int key_bf16, value_bf16, value_mode, query_bf16;
+  int key_nib;                 // 3- or 4-bit base codes (one per nibble)
   double kappa;                // scale of the side correction in s_hat
   const void* q;
   const void* k_ref;           // reference keys (key dtype), element strides below
@@ -159,6 +167,7 @@ struct PrefillArgs {
   int64_t start, n_q;          // query token t sits at position start + t; the cache holds
                                // tokens [0, start + n_q) (whole groups, the rest in the tails)
   int query_bf16, key_bf16, value_bf16, value_mode, out_bf16;
+  int key_nib;                 // 3- or 4-bit base codes (one per nibble)
   float corr_scale;
   const void* q;               // [B][n_q][Hq][d]
   const uint8_t* kcode;

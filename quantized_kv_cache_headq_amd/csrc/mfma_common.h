@@ -17,6 +17,7 @@ typedef float float2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 
 template <class T, class S>
 __device__ __forceinline__ T bitcast(const S& s) {
@@ -42,6 +43,14 @@ __device__ __forceinline__ uint32_t fp4_pair_bf16(uint32_t m) {
 __device__ __forceinline__ half8_t key_codes8(uint32_t m) {
   const u32x4 w = {fp4_pair_f16<0>(m), fp4_pair_f16<1>(m), fp4_pair_f16<2>(m), fp4_pair_f16<3>(m)};
   return bitcast<half8_t>(w);
+}
+// 8 key codes (f16) of a nibble word (3- and 4-bit base codes): the channel pair (2i, 2i+1) is
+// nibble i of the low and the high half; or-ing 0x6400 makes each half 1024 + code exactly.
+__device__ __forceinline__ half8_t key_codes8_nib(uint32_t w) {
+  u32x4 p;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) p[i] = ((w >> (4 * i)) & 0x000F000Fu) | 0x64006400u;
+  return bitcast<half8_t>(p) - (half8_t)(_Float16)1024.0f;
 }
 // 8 value codes (bf16) of one channel tile from a word of the lane's value codes: the low 16 bits
 // are tile 2w, the high 16 bits tile 2w+1; even-masked bytes hold token items 0..3, odd-masked

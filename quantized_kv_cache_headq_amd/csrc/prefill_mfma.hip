@@ -38,9 +38,9 @@ constexpr float kLazyMax = 8.0f;          // rescale only when the max grows by 
 // the cache): packed key codes 32 x d/4 | key step/zero rows 2 x d x 2 | side codes 32 x r/2 |
 // sigma 32 x 2 | (2-bit values) value step/zero rows 2 x d/32 x 32 x 2 | values (dense bf16
 // [d][32], or 2-bit codes d x 8 in matrix-operand order).
-template <int D, int R, bool VQ2>
+template <int D, int R, bool VQ2, bool NB>
 struct Tile {
-  static constexpr int KC = kGroup * D / 4, KM = 4 * D, SC = kGroup * R / 2, SG = R > 0 ? kGroup * 2 : 0;
+  static constexpr int KC = kGroup * D / (NB ? 2 : 4), KM = 4 * D, SC = kGroup * R / 2, SG = R > 0 ? kGroup * 2 : 0;
   static constexpr int VM = VQ2 ? 4 * D : 0, VB = VQ2 ? D * 8 : D * kGroup * 2;
   static constexpr int OFF_KM = KC, OFF_SC = OFF_KM + KM, OFF_SG = OFF_SC + SC, OFF_VM = OFF_SG + SG;
   static constexpr int OFF_V = OFF_VM + VM, BYTES = OFF_V + VB;
@@ -49,9 +49,9 @@ struct Tile {
 };
 
 // Source of the i-th 16-byte chunk of group gi of stream (b, h).
-template <int D, int R, bool VQ2>
+template <int D, int R, bool VQ2, bool NB>
 __device__ __forceinline__ const u32x4* chunk_src(const PrefillArgs& a, int64_t blk, int i) {
-  using TL = Tile<D, R, VQ2>;
+  using TL = Tile<D, R, VQ2, NB>;
   int off = 16 * i;
   if (off < TL::KC) return reinterpret_cast<const u32x4*>(a.kcode + blk * TL::KC + off);
   off -= TL::KC;
@@ -78,25 +78,23 @@ struct Fixed {
 };
 
 // One staged group against the wave's 16 columns: scores, causal mask, online softmax, P.V.
-template <int D, int R, bool VQ2>
+template <int D, int R, bool VQ2, bool NB>
 __device__ __forceinline__ void group_step(const uint8_t* T, const Fixed<D, R>& f, float kappa, int tok0,
                                            bool masked, int n_att, float* lg_row, int n, int quad, int lane,
                                            floatx4* o_acc, float* z_acc, float& m_run, float& l_run) {
-  using TL = Tile<D, R, VQ2>;
+  using TL = Tile<D, R, VQ2, NB>;
   constexpr int NKT = D / 32, NCT = D / 16, NG = D / 32;
   const _Float16* km_h = reinterpret_cast<const _Float16*>(T + TL::OFF_KM);
   const int row_tok0 = 8 * (n / 4) + (n % 4);  // token of this lane's row in tile 0 (tile 1: +4)
-  uint32_t kcw[2][D / 64];                      // packed codes of the row tokens, this lane's piece
+  // packed codes of the row tokens, this lane's piece (channels (d/4)*quad .. +d/4): d/64 words
+  // of 2-bit codes, or d/32 nibble words (3- and 4-bit base codes)
+  constexpr int KW = NB ? D / 32 : D / 64;
+  uint32_t kcw[2][KW];
 #pragma unroll
   for (int Ti = 0; Ti < 2; ++Ti) {
-    const uint8_t* p = T + (row_tok0 + 4 * Ti) * (D / 4) + (D / 16) * quad;
-    if constexpr (D == 128) {
-      const u32x2 w = *reinterpret_cast<const u32x2*>(p);
-      kcw[Ti][0] = w[0];
-      kcw[Ti][1] = w[1];
-    } else {
-      kcw[Ti][0] = *reinterpret_cast<const uint32_t*>(p);
-    }
+    const uint8_t* p = T + (row_tok0 + 4 * Ti) * (TL::KC / 32) + 4 * KW * quad;
+#pragma unroll
+    for (int w = 0; w < KW; ++w) kcw[Ti][w] = reinterpret_cast<const uint32_t*>(p)[w];
   }
   // zero term q.z (the same for every token row), then codes . (q o s) on top of it
   floatx4 cz = (floatx4){0.f, 0.f, 0.f, 0.f};
@@ -118,8 +116,13 @@ __device__ __forceinline__ void group_step(const uint8_t* T, const Fixed<D, R>& 
     const half8_t p_lo = __builtin_elementwise_fma(f.bq_lo[t], st[t], e);
 #pragma unroll
     for (int Ti = 0; Ti < 2; ++Ti) {
-      const uint32_t w = kcw[Ti][(D == 128) ? (t >> 1) : 0];
-      const half8_t ac = key_codes8((t & 1) ? odd_codes(w) : even_codes(w));
+      half8_t ac;
+      if constexpr (NB) {
+        ac = key_codes8_nib(kcw[Ti][t]);
+      } else {
+        const uint32_t w = kcw[Ti][(D == 128) ? (t >> 1) : 0];
+        ac = key_codes8((t & 1) ? odd_codes(w) : even_codes(w));
+      }
       acc[Ti] = mfma_f16(ac, p_hi, acc[Ti]);
       acc[Ti] = mfma_f16(ac, p_lo, acc[Ti]);
     }
@@ -347,9 +350,9 @@ __device__ __forceinline__ void tail_step(const PrefillArgs& a, int64_t bh, int6
   }
 }
 
-template <int D, int R, bool VQ2>
+template <int D, int R, bool VQ2, bool NB>
 __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
-  using TL = Tile<D, R, VQ2>;
+  using TL = Tile<D, R, VQ2, NB>;
   constexpr int RU = R > 0 ? R : 1;
   constexpr int NKT = D / 32, NCT = D / 16, NG = D / 32;
   constexpr int NPF = (TL::CHUNKS + kThreads - 1) / kThreads;  // staged chunks per thread
@@ -460,7 +463,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
 #pragma unroll
     for (int k = 0; k < NPF; ++k) {
       const int i = tid + k * kThreads;
-      if (i < TL::CHUNKS) pf[k] = *chunk_src<D, R, VQ2>(a, blk, i);
+      if (i < TL::CHUNKS) pf[k] = *chunk_src<D, R, VQ2, NB>(a, blk, i);
     }
   };
   auto stage_group = [&](int buf) {
@@ -480,7 +483,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
     if (gi + 1 < G) fetch_group(gi + 1);  // in flight while this group is computed
     const int64_t tok0 = gi * kGroup;
     if (tok0 < att_max_w)
-      group_step<D, R, VQ2>(reinterpret_cast<const uint8_t*>(tile_s[cur]), f, a.corr_scale, (int)tok0,
+      group_step<D, R, VQ2, NB>(reinterpret_cast<const uint8_t*>(tile_s[cur]), f, a.corr_scale, (int)tok0,
                             tok0 + kGroup > att_min_w, (int)n_att, lg_row, n, quad, lane, o_acc, z_acc, m_run,
                             l_run);
     if (gi + 1 < G) stage_group(cur ^ 1);
@@ -524,16 +527,16 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
   }
 }
 
-template <int D, bool VQ2>
+template <int D, bool VQ2, bool NB>
 hipError_t launch_r(const PrefillArgs& a, hipStream_t s) {
   const int64_t n_cols = a.n_q * a.gqa;
   dim3 grid((unsigned)((n_cols + kCols - 1) / kCols), (unsigned)a.hkv, (unsigned)a.batch);
   switch (a.r) {
-    case 0: hipLaunchKernelGGL((prefill_mfma_kernel<D, 0, VQ2>), grid, dim3(kThreads), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((prefill_mfma_kernel<D, 4, VQ2>), grid, dim3(kThreads), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((prefill_mfma_kernel<D, 8, VQ2>), grid, dim3(kThreads), 0, s, a); break;
-    case 16: hipLaunchKernelGGL((prefill_mfma_kernel<D, 16, VQ2>), grid, dim3(kThreads), 0, s, a); break;
-    case 32: hipLaunchKernelGGL((prefill_mfma_kernel<D, 32, VQ2>), grid, dim3(kThreads), 0, s, a); break;
+    case 0: hipLaunchKernelGGL((prefill_mfma_kernel<D, 0, VQ2, NB>), grid, dim3(kThreads), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((prefill_mfma_kernel<D, 4, VQ2, NB>), grid, dim3(kThreads), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((prefill_mfma_kernel<D, 8, VQ2, NB>), grid, dim3(kThreads), 0, s, a); break;
+    case 16: hipLaunchKernelGGL((prefill_mfma_kernel<D, 16, VQ2, NB>), grid, dim3(kThreads), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((prefill_mfma_kernel<D, 32, VQ2, NB>), grid, dim3(kThreads), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -543,8 +546,13 @@ hipError_t launch_r(const PrefillArgs& a, hipStream_t s) {
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
   const bool q2 = a.value_mode == HEADQ_V_Q2;
-  if (a.d == 64) return q2 ? launch_r<64, true>(a, s) : launch_r<64, false>(a, s);
-  if (a.d == 128) return q2 ? launch_r<128, true>(a, s) : launch_r<128, false>(a, s);
+  if (a.key_nib) {
+    if (a.d == 64) return q2 ? launch_r<64, true, true>(a, s) : launch_r<64, false, true>(a, s);
+    if (a.d == 128) return q2 ? launch_r<128, true, true>(a, s) : launch_r<128, false, true>(a, s);
+  } else {
+    if (a.d == 64) return q2 ? launch_r<64, true, false>(a, s) : launch_r<64, false, false>(a, s);
+    if (a.d == 128) return q2 ? launch_r<128, true, false>(a, s) : launch_r<128, false, false>(a, s);
+  }
   return hipErrorInvalidValue;
 }
 

@@ -25,7 +25,7 @@ def config(w: synth.Workload, batch=None, cap=None):
     return hq.Config(head_dim=w.head_dim, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads,
                      batch=w.batch if batch is None else batch, capacity=w.n_ctx if cap is None else cap,
                      rank=w.rank, key_dtype=DT[w.key_dtype], value_dtype=DT[w.value_dtype],
-                     value_mode=VMODE[w.value_mode], query_dtype=DT[w.query_dtype])
+                     value_mode=VMODE[w.value_mode], query_dtype=DT[w.query_dtype], base_bits=w.base_bits)
 
 
 def torch_dtype(name):

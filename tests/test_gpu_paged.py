@@ -62,7 +62,7 @@ def _run(w, B, cap, steps, out_bf16=False, n_splits=0, seed=11):
     if w.rank:
         pc.set_basis(U)
     oc = orc.empty_cache(B, w.n_kv_heads, cap, w.head_dim, w.rank, VMODE[w.value_mode], VDT[w.value_dtype],
-                         key_dtype=VDT[w.key_dtype])
+                         key_dtype=VDT[w.key_dtype], base_bits=w.base_bits)
     lengths = np.array([(7 * b) % 32 for b in range(B)])  # rows start at different offsets
     for n_new in steps:
         K = np.stack([Kf[b, :, lengths[b]:lengths[b] + n_new] for b in range(B)])
@@ -72,7 +72,8 @@ def _run(w, B, cap, steps, out_bf16=False, n_splits=0, seed=11):
         for b in range(B):
             for h in range(w.n_kv_heads):
                 orc.write_stream(oc, b, h, int(lengths[b]), K[b, h], value_payload(V[b, h], w),
-                                 None if U is None else U[h], VMODE[w.value_mode], VDT[w.value_dtype])
+                                 None if U is None else U[h], VMODE[w.value_mode], VDT[w.value_dtype],
+                                 bits=w.base_bits)
         lengths = lengths + n_new
         compare_cache(_gathered(pc, table, G), oc)
         n_max = int(lengths.max())

@@ -33,7 +33,7 @@ def _build(w, U, K, V, n_ctx):
     n_full = n_ctx // 32 * 32
     cap = (n_ctx + 31) // 32 * 32
     c = orc.empty_cache(B, H, cap, w.head_dim, 0 if U is None else U.shape[2], VMODE[w.value_mode],
-                        VDT[w.value_dtype], key_dtype=VDT[w.key_dtype])
+                        VDT[w.value_dtype], key_dtype=VDT[w.key_dtype], base_bits=w.base_bits)
     enc = {}
     for b in range(B):
         for h in range(H):
@@ -41,10 +41,10 @@ def _build(w, U, K, V, n_ctx):
             vm, vd = VMODE[w.value_mode], VDT[w.value_dtype]
             if n_full:
                 enc[(b, h)] = orc.write_stream(c, b, h, 0, K[b, h, :n_full], value_payload(V[b, h, :n_full], w), Uh,
-                                               vm, vd)
+                                               vm, vd, bits=w.base_bits)
             if n_ctx > n_full:
                 orc.write_stream(c, b, h, n_full, K[b, h, n_full:n_ctx], value_payload(V[b, h, n_full:n_ctx], w), Uh,
-                                 vm, vd)
+                                 vm, vd, bits=w.base_bits)
     return c
 
 
