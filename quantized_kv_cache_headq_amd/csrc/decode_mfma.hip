@@ -211,17 +211,11 @@ struct Fixed {
   float kappa;                     // corr_scale
 };
 
-// One 32-token group: scores, online-softmax update, P.V accumulation.
+// Stage the lane's raw bytes of one group into a wave's LDS slot (the caller orders the slot's
+// accesses with wave fences: lanes read what other lanes wrote).
 template <int D, int R, bool VQ2, bool NB>
-__device__ __forceinline__ void process_group(const GroupRaw<D, R, VQ2, NB>& cur, const Fixed<D, R>& f, uint8_t* slot,
-                                              const DecodeArgs& a, int gi, int b, int hq0, int g, int lane, int n,
-                                              int quad, floatx4* o_acc, float* z_acc, float& m_run, float& l_run) {
-  constexpr int NKT = D / 32, NCT = D / 16, NG = D / 32;
+__device__ __forceinline__ void stage_group(const GroupRaw<D, R, VQ2, NB>& cur, uint8_t* slot, int lane) {
   using KS = KSide<D, R, VQ2, NB>;
-  // Staged bytes through the wave's LDS slot. Lanes read what other lanes wrote, so the accesses
-  // are ordered by wave-scope fences (the wave executes its LDS operations in order; the fences
-  // stop the compiler from moving reads across the writes, in either direction).
-  lds_wave_fence();
   *reinterpret_cast<typename Bytes<KS::KC / 64>::T*>(slot + lane * (KS::KC / 64)) = cur.kc;
   *reinterpret_cast<typename Bytes<D / 16>::T*>(slot + KS::OFF_KM + lane * (D / 16)) = cur.km;
   if constexpr (R > 0) {
@@ -229,7 +223,33 @@ __device__ __forceinline__ void process_group(const GroupRaw<D, R, VQ2, NB>& cur
     slot[KS::OFF_SG + lane] = cur.sg;
   }
   if constexpr (VQ2) *reinterpret_cast<typename Bytes<D / 16>::T*>(slot + KS::OFF_VM + lane * (D / 16)) = cur.vm;
-  lds_wave_fence();
+}
+
+// (q o s) at this lane's channels as hi + lo f16 operands (exact product error by fma, plus the
+// low part of q times s), s the key step row of the group staged in `slot`.
+template <int D, int R, bool VQ2, bool NB>
+__device__ __forceinline__ void query_times_step(const uint8_t* slot, const Fixed<D, R>& f, int quad, half8_t* p_hi,
+                                                 half8_t* p_lo) {
+  using KS = KSide<D, R, VQ2, NB>;
+  const _Float16* km_h = reinterpret_cast<const _Float16*>(slot + KS::OFF_KM);
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t) {
+    const half8_t st = *reinterpret_cast<const half8_t*>(km_h + (D / 4) * quad + 8 * t);
+    p_hi[t] = f.bq_hi[t] * st;
+    const half8_t e = __builtin_elementwise_fma(f.bq_hi[t], st, -p_hi[t]);
+    p_lo[t] = __builtin_elementwise_fma(f.bq_lo[t], st, e);
+  }
+}
+
+// Raw logit parts of the 32 tokens of the group staged in `slot` against the B operands of this
+// lane's column: acc = q.z + codes.(q o s) and cr = zc.(U^T q), token tiles T = 0, 1. PRE: q o s
+// is given (p_hi/p_lo, from query_times_step); otherwise it is formed here, k-tile by k-tile, from
+// the step row of the same group.
+template <int D, int R, bool VQ2, bool NB, bool PRE>
+__device__ __forceinline__ void group_logits(const uint8_t* slot, const Fixed<D, R>& f, const half8_t* p_hi,
+                                             const half8_t* p_lo, int n, int quad, floatx4* acc, floatx4* cr) {
+  constexpr int NKT = D / 32;
+  using KS = KSide<D, R, VQ2, NB>;
   const _Float16* km_h = reinterpret_cast<const _Float16*>(slot + KS::OFF_KM);
   const int row_tok0 = 8 * (n / 4) + (n % 4);  // token of this lane's row in tile 0 (tile 1: +4)
   // packed codes of the row tokens, this lane's piece (channels (d/4)*quad .. +d/4): d/64 words
@@ -242,25 +262,30 @@ __device__ __forceinline__ void process_group(const GroupRaw<D, R, VQ2, NB>& cur
 #pragma unroll
     for (int w = 0; w < KW; ++w) kcw[T][w] = reinterpret_cast<const uint32_t*>(p)[w];
   }
-
   // zero term q.z (identical for every token row), then codes . (q o s) on top of it
   floatx4 cz = (floatx4){0.f, 0.f, 0.f, 0.f};
   half8_t st[NKT];
 #pragma unroll
   for (int t = 0; t < NKT; ++t) {
     const int c0 = (D / 4) * quad + 8 * t;
-    st[t] = *reinterpret_cast<const half8_t*>(km_h + c0);
+    if constexpr (!PRE) st[t] = *reinterpret_cast<const half8_t*>(km_h + c0);
     const half8_t zt = *reinterpret_cast<const half8_t*>(km_h + D + c0);
     cz = mfma_f16(zt, f.bq_hi[t], cz);
     cz = mfma_f16(zt, f.bq_lo[t], cz);
   }
-  floatx4 acc[2] = {cz, cz};
+  acc[0] = cz;
+  acc[1] = cz;
 #pragma unroll
   for (int t = 0; t < NKT; ++t) {
-    // (q o s) as hi + lo f16: exact product error by fma, plus the low part of q times s
-    const half8_t p_hi = f.bq_hi[t] * st[t];
-    const half8_t e = __builtin_elementwise_fma(f.bq_hi[t], st[t], -p_hi);
-    const half8_t p_lo = __builtin_elementwise_fma(f.bq_lo[t], st[t], e);
+    half8_t ph, pl;
+    if constexpr (PRE) {
+      ph = p_hi[t];
+      pl = p_lo[t];
+    } else {
+      ph = f.bq_hi[t] * st[t];
+      const half8_t e = __builtin_elementwise_fma(f.bq_hi[t], st[t], -ph);
+      pl = __builtin_elementwise_fma(f.bq_lo[t], st[t], e);
+    }
 #pragma unroll
     for (int T = 0; T < 2; ++T) {
       // k-tile t covers channels (d/4)*quad + 8t .. +7: the even (t even) or odd (t odd) run of
@@ -272,13 +297,11 @@ __device__ __forceinline__ void process_group(const GroupRaw<D, R, VQ2, NB>& cur
         const uint32_t w = kcw[T][(D == 128) ? (t >> 1) : 0];
         ac = key_codes8((t & 1) ? odd_codes(w) : even_codes(w));
       }
-      acc[T] = mfma_f16(ac, p_hi, acc[T]);
-      acc[T] = mfma_f16(ac, p_lo, acc[T]);
+      acc[T] = mfma_f16(ac, ph, acc[T]);
+      acc[T] = mfma_f16(ac, pl, acc[T]);
     }
   }
-  float sv[8];  // scores (log2 units) of tokens 8*quad + j for head n
   if constexpr (R > 0) {
-    floatx4 cr[2];
 #pragma unroll
     for (int T = 0; T < 2; ++T) {
       cr[T] = (floatx4){0.f, 0.f, 0.f, 0.f};
@@ -297,6 +320,16 @@ __device__ __forceinline__ void process_group(const GroupRaw<D, R, VQ2, NB>& cur
         cr[T] = mfma_f16k16(az, f.bu_lo4, cr[T]);
       }
     }
+  }
+}
+
+// Scores (log2 units) of tokens 8*quad + j for this lane's column: the corrected logit
+// inv_scale * (acc + kappa * sigma_j * cr), sigma from the group staged in `slot`.
+template <int D, int R, bool VQ2, bool NB>
+__device__ __forceinline__ void group_scores(const uint8_t* slot, const Fixed<D, R>& f, int quad, const floatx4* acc,
+                                             const floatx4* cr, float* sv) {
+  using KS = KSide<D, R, VQ2, NB>;
+  if constexpr (R > 0) {
     const half8_t sg = *reinterpret_cast<const half8_t*>(slot + KS::OFF_SG + 16 * quad);
 #pragma unroll
     for (int T = 0; T < 2; ++T)
@@ -309,22 +342,24 @@ __device__ __forceinline__ void process_group(const GroupRaw<D, R, VQ2, NB>& cur
 #pragma unroll
       for (int j = 0; j < 4; ++j) sv[4 * T + j] = f.inv_scale * acc[T][j];
   }
-  if (a.logits_dbg && n < g) {
-    float* dst = a.logits_dbg + ((int64_t)b * a.hq + hq0 + n) * a.n_ctx + (int64_t)gi * kGroup + 8 * quad;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) dst[j] = sv[j] * kLn2;
-  }
+}
 
-  // online softmax (lazy maximum)
+// Online-softmax step (lazy maximum) over this lane's 8 scores; p = 2^(s - m_run), with live =
+// false giving p = 0 and no update (a column whose group does not exist in this step).
+template <int NCT, int NG, bool VQ2>
+__device__ __forceinline__ void softmax_step(const float* sv, bool live, float* p, floatx4* o_acc, float* z_acc,
+                                             float& m_run, float& l_run) {
   float mx = sv[0];
 #pragma unroll
   for (int j = 1; j < 8; ++j) mx = fmaxf(mx, sv[j]);
   mx = fmaxf(mx, __shfl_xor(mx, 16));
   mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const bool grow = mx > m_run + kLazyMax;  // true on the first group (m_run = -inf)
+  const bool grow = live && mx > m_run + kLazyMax;  // true on the first group (m_run = -inf)
   if (__any(grow)) {
+    // alpha: 0 on a column's first group; exactly 1 for the columns that keep their maximum
+    // (also those still at -inf, whose state is all zero)
     const float m_new = grow ? mx : m_run;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first group, 1 if unchanged
+    const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
     m_run = m_new;
     l_run *= alpha;
 #pragma unroll
@@ -333,81 +368,179 @@ __device__ __forceinline__ void process_group(const GroupRaw<D, R, VQ2, NB>& cur
 #pragma unroll
       for (int cg = 0; cg < NG; ++cg) z_acc[cg] *= alpha;
   }
-  float p[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    p[j] = __builtin_amdgcn_exp2f(sv[j] - m_run);  // v_exp_f32; results below 2^-126 flush to 0
+    p[j] = live ? __builtin_amdgcn_exp2f(sv[j] - m_run) : 0.0f;  // v_exp_f32; below 2^-126 flushes to 0
     l_run += p[j];
   }
-  if constexpr (VQ2) {
-    // v_hat = code * s + z per (token, 32-channel group): the code part is a matrix product with
-    // p o s as the second operand (one per channel group), the zero part sum_j p_j z_j per head
-    // and group is accumulated per lane (tokens 8*quad .. +7) and summed over the quads at the end.
-    const _Float16* vm_h = reinterpret_cast<const _Float16*>(slot + KS::OFF_VM);
-    uint32_t ve[NG], vo[NG];
+}
+
+// 2-bit values, the B side of this lane's column: p o s as bf16 hi/lo pairs per 32-channel group
+// (the code part of v_hat = code * s + z is a matrix product with p o s as second operand), and
+// the zero part sum_j p_j z_j per channel group accumulated per lane (tokens 8*quad .. +7; the
+// quads are summed at the end). s and z come from the group staged in `slot`.
+template <int D, int R, bool NB>
+__device__ __forceinline__ void value_operands(const uint8_t* slot, const float* p, int quad, bf16x8_t* bh,
+                                               bf16x8_t* bl, float* z_acc) {
+  constexpr int NG = D / 32;
+  using KS = KSide<D, R, true, NB>;
+  const _Float16* vm_h = reinterpret_cast<const _Float16*>(slot + KS::OFF_VM);
 #pragma unroll
-    for (int w = 0; w < NG; ++w) {
-      const uint32_t x = word_of<D / 8>(cur.vc, w);
-      ve[w] = even_codes(x);
-      vo[w] = odd_codes(x);
+  for (int cg = 0; cg < NG; ++cg) {
+    const half8_t s8 = *reinterpret_cast<const half8_t*>(vm_h + cg * kGroup + 8 * quad);
+    const half8_t z8 = *reinterpret_cast<const half8_t*>(vm_h + (NG + cg) * kGroup + 8 * quad);
+    u32x4 xh, xl;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t h2, l2;
+      // fma with a zero addend maps to one mixed-precision fma (the f16 step read directly)
+      split_bf16_pair(__builtin_fmaf(p[2 * i], (float)s8[2 * i], 0.0f),
+                      __builtin_fmaf(p[2 * i + 1], (float)s8[2 * i + 1], 0.0f), h2, l2);
+      xh[i] = h2;
+      xl[i] = l2;
     }
+    float za = z_acc[cg];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) za = fmaf(p[j], (float)z8[j], za);
+    z_acc[cg] = za;
+    bh[cg] = bitcast<bf16x8_t>(xh);
+    bl[cg] = bitcast<bf16x8_t>(xl);
+  }
+}
+
+// One 32-token group: scores, online-softmax update, P.V accumulation.
+template <int D, int R, bool VQ2, bool NB>
+__device__ __forceinline__ void process_group(const GroupRaw<D, R, VQ2, NB>& cur, const Fixed<D, R>& f, uint8_t* slot,
+                                              const DecodeArgs& a, int gi, int b, int hq0, int g, int lane, int n,
+                                              int quad, floatx4* o_acc, float* z_acc, float& m_run, float& l_run) {
+  constexpr int NKT = D / 32, NCT = D / 16, NG = D / 32;
+  lds_wave_fence();
+  stage_group<D, R, VQ2, NB>(cur, slot, lane);
+  lds_wave_fence();
+  floatx4 acc[2], cr[2];
+  group_logits<D, R, VQ2, NB, false>(slot, f, nullptr, nullptr, n, quad, acc, cr);
+  float sv[8];  // scores (log2 units) of tokens 8*quad + j for head n
+  group_scores<D, R, VQ2, NB>(slot, f, quad, acc, cr, sv);
+  if (a.logits_dbg && n < g) {
+    float* dst = a.logits_dbg + ((int64_t)b * a.hq + hq0 + n) * a.n_ctx + (int64_t)gi * kGroup + 8 * quad;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) dst[j] = sv[j] * kLn2;
+  }
+  float p[8];
+  softmax_step<NCT, NG, VQ2>(sv, true, p, o_acc, z_acc, m_run, l_run);
+  if constexpr (VQ2) {
+    bf16x8_t bh[NG], bl[NG];
+    value_operands<D, R, NB>(slot, p, quad, bh, bl, z_acc);
 #pragma unroll
     for (int cg = 0; cg < NG; ++cg) {
-      const half8_t s8 = *reinterpret_cast<const half8_t*>(vm_h + cg * kGroup + 8 * quad);
-      const half8_t z8 = *reinterpret_cast<const half8_t*>(vm_h + (NG + cg) * kGroup + 8 * quad);
-      u32x4 xh, xl;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint32_t h2, l2;
-        // fma with a zero addend maps to one mixed-precision fma (the f16 step read directly)
-        split_bf16_pair(__builtin_fmaf(p[2 * i], (float)s8[2 * i], 0.0f),
-                        __builtin_fmaf(p[2 * i + 1], (float)s8[2 * i + 1], 0.0f), h2, l2);
-        xh[i] = h2;
-        xl[i] = l2;
-      }
-      float za = z_acc[cg];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) za = fmaf(p[j], (float)z8[j], za);
-      z_acc[cg] = za;
-      const bf16x8_t bh = bitcast<bf16x8_t>(xh), bl = bitcast<bf16x8_t>(xl);
       // tiles 2cg and 2cg+1 = the low and high halves of the lane's code word cg
-      const bf16x8_t a0 = value_codes8<0>(ve[cg], vo[cg]);
-      const bf16x8_t a1 = value_codes8<1>(ve[cg], vo[cg]);
-      o_acc[2 * cg] = mfma_bf16(a0, bh, o_acc[2 * cg]);
-      o_acc[2 * cg] = mfma_bf16(a0, bl, o_acc[2 * cg]);
-      o_acc[2 * cg + 1] = mfma_bf16(a1, bh, o_acc[2 * cg + 1]);
-      o_acc[2 * cg + 1] = mfma_bf16(a1, bl, o_acc[2 * cg + 1]);
+      const uint32_t x = word_of<D / 8>(cur.vc, cg);
+      const uint32_t ve = even_codes(x), vo = odd_codes(x);
+      const bf16x8_t a0 = value_codes8<0>(ve, vo);
+      const bf16x8_t a1 = value_codes8<1>(ve, vo);
+      o_acc[2 * cg] = mfma_bf16(a0, bh[cg], o_acc[2 * cg]);
+      o_acc[2 * cg] = mfma_bf16(a0, bl[cg], o_acc[2 * cg]);
+      o_acc[2 * cg + 1] = mfma_bf16(a1, bh[cg], o_acc[2 * cg + 1]);
+      o_acc[2 * cg + 1] = mfma_bf16(a1, bl[cg], o_acc[2 * cg + 1]);
     }
   } else {
-    bf16x8_t p_hi, p_lo;
+    bf16x8_t p_hi8, p_lo8;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const __bf16 ph = (__bf16)p[j];
-      p_hi[j] = ph;
-      p_lo[j] = (__bf16)(p[j] - (float)ph);
+      p_hi8[j] = ph;
+      p_lo8[j] = (__bf16)(p[j] - (float)ph);
     }
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       const bf16x8_t av = bitcast<bf16x8_t>(cur.v[ct]);
-      o_acc[ct] = mfma_bf16(av, p_hi, o_acc[ct]);
-      o_acc[ct] = mfma_bf16(av, p_lo, o_acc[ct]);
+      o_acc[ct] = mfma_bf16(av, p_hi8, o_acc[ct]);
+      o_acc[ct] = mfma_bf16(av, p_lo8, o_acc[ct]);
+    }
+  }
+}
+
+// J groups of one step (2-bit values, g <= 16 / J) share the 16 matrix columns: column n = lane
+// % 16 belongs to block jl = n / g, head hd = n % g, and follows group jl of the step. Each
+// group's products run over all 16 columns and every lane keeps the result of its own group, so
+// the per-column work (q o s, the softmax step, p o s and its split) is done once per step
+// instead of once per group; the matrix products per group are unchanged. The columns of a head
+// are separate online-softmax partials, merged with the waves' partials at the end. `nv` groups
+// of the step exist (the last step of a wave may hold fewer); the others' columns stay idle: the
+// products of all J groups run unconditionally (straight-line code the scheduler can interleave),
+// a missing group's results are only ever selected by idle columns, whose scores are replaced and
+// whose probabilities are 0, and its value operand meets zero columns only.
+template <int D, int R, bool NB, int J>
+__device__ __forceinline__ void process_block(const typename Bytes<D / 8>::T* vcs, const int* gis, int nv,
+                                              const Fixed<D, R>& f, const uint8_t* slots, const DecodeArgs& a, int b,
+                                              int hq0, int g, int jl, int hd, int n, int quad, floatx4* o_acc,
+                                              float* z_acc, float& m_run, float& l_run) {
+  constexpr int NKT = D / 32, NCT = D / 16, NG = D / 32;
+  using KS = KSide<D, R, true, NB>;
+  const bool live = jl < nv;
+  // the lane's own group (idle columns read the last existing one: finite bytes, weight 0)
+  const uint8_t* own = slots + (live ? jl : nv - 1) * KS::BYTES;
+  half8_t p_hi[NKT], p_lo[NKT];
+  query_times_step<D, R, true, NB>(own, f, quad, p_hi, p_lo);
+  floatx4 A[2], C[2];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    floatx4 acc[2], cr[2];
+    group_logits<D, R, true, NB, true>(slots + j * KS::BYTES, f, p_hi, p_lo, n, quad, acc, cr);
+#pragma unroll
+    for (int T = 0; T < 2; ++T) {
+      A[T] = (j == 0 || jl == j) ? acc[T] : A[T];
+      if constexpr (R > 0) C[T] = (j == 0 || jl == j) ? cr[T] : C[T];
+    }
+  }
+  float sv[8];
+  group_scores<D, R, true, NB>(own, f, quad, A, C, sv);
+  if (a.logits_dbg && live && hd < g) {
+    int gi = gis[0];
+#pragma unroll
+    for (int j = 1; j < J; ++j) gi = jl == j ? gis[j] : gi;
+    float* dst = a.logits_dbg + ((int64_t)b * a.hq + hq0 + hd) * a.n_ctx + (int64_t)gi * kGroup + 8 * quad;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) dst[j] = sv[j] * kLn2;
+  }
+  float p[8];
+  softmax_step<NCT, NG, true>(sv, live, p, o_acc, z_acc, m_run, l_run);
+  bf16x8_t bh[NG], bl[NG];
+  value_operands<D, R, NB>(own, p, quad, bh, bl, z_acc);
+  const bf16x8_t zero8 = bitcast<bf16x8_t>((u32x4){0u, 0u, 0u, 0u});
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+#pragma unroll
+    for (int cg = 0; cg < NG; ++cg) {
+      // group j's value codes against the columns of block j only
+      const bf16x8_t bhj = jl == j ? bh[cg] : zero8, blj = jl == j ? bl[cg] : zero8;
+      const uint32_t x = word_of<D / 8>(vcs[j], cg);
+      const uint32_t ve = even_codes(x), vo = odd_codes(x);
+      const bf16x8_t a0 = value_codes8<0>(ve, vo);
+      const bf16x8_t a1 = value_codes8<1>(ve, vo);
+      o_acc[2 * cg] = mfma_bf16(a0, bhj, o_acc[2 * cg]);
+      o_acc[2 * cg] = mfma_bf16(a0, blj, o_acc[2 * cg]);
+      o_acc[2 * cg + 1] = mfma_bf16(a1, bhj, o_acc[2 * cg + 1]);
+      o_acc[2 * cg + 1] = mfma_bf16(a1, blj, o_acc[2 * cg + 1]);
     }
   }
 }
 
 // The unfinished last group: n_ctx % 32 tokens whose keys and values are held exactly in the
-// tails (no base or side code). On the vector units, once per stream: lane (n, quad) scores tokens
-// 8*quad .. +7 for head n with the scaled query, takes the same online-softmax step as a group, and
-// adds p . v to its own output channels 16*ct + 4*quad + j, fetching the other quads'
-// probabilities by lane shuffles.
+// tails (no base or side code). On the vector units, once per stream: lane (column n, quad)
+// scores tokens 8*quad .. +7 for its head hd with the scaled query, takes the same online-softmax
+// step as a group, and adds p . v to its own output channels 16*ct + 4*quad + j, fetching the
+// other quads' probabilities by lane shuffles. Columns with act = false (the other blocks of a
+// packed layout, whose heads the first block already covers) take no part.
 template <int D>
 __device__ __forceinline__ void process_tail(const DecodeArgs& a, int64_t n_ctx, int64_t bh, int b, int hq0, int g,
-                                             int n,
-                                             int quad, const float (*qs)[D], float inv_scale, floatx4* o_acc,
-                                             float* z_acc, int n_z, float& m_run, float& l_run) {
+                                             int n, int hd, bool act, int quad, const float (*qs)[D],
+                                             float inv_scale, floatx4* o_acc, float* z_acc, int n_z, float& m_run,
+                                             float& l_run) {
   constexpr int NCT = D / 16;
   const int64_t n_full = n_ctx / kGroup * kGroup;
   const int tail_len = (int)(n_ctx - n_full);
+  const int own_len = act ? tail_len : 0;  // rows this lane scores
   // scores of rows 8*quad + j: channels in steps of 8 (one 16-byte or two 16-byte loads per row)
   float acc[8];
 #pragma unroll
@@ -417,7 +550,7 @@ __device__ __forceinline__ void process_tail(const DecodeArgs& a, int64_t n_ctx,
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int t = 8 * quad + j;
-      if (t >= tail_len) continue;
+      if (t >= own_len) continue;
       const int64_t row = (bh * kGroup + t) * D + c;
       float k[8];
       if (a.key_bf16) {
@@ -437,16 +570,16 @@ __device__ __forceinline__ void process_tail(const DecodeArgs& a, int64_t n_ctx,
         }
       }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[j] = fmaf(qs[n][c + i], k[i], acc[j]);
+      for (int i = 0; i < 8; ++i) acc[j] = fmaf(qs[hd][c + i], k[i], acc[j]);
     }
   }
   float sv[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int t = 8 * quad + j;
-    sv[j] = t < tail_len ? inv_scale * acc[j] : -INFINITY;
-    if (t < tail_len && a.logits_dbg && n < g)
-      a.logits_dbg[((int64_t)b * a.hq + hq0 + n) * a.n_ctx + n_full + t] = sv[j] * kLn2;
+    sv[j] = t < own_len ? inv_scale * acc[j] : -INFINITY;
+    if (t < own_len && a.logits_dbg && hd < g)
+      a.logits_dbg[((int64_t)b * a.hq + hq0 + hd) * a.n_ctx + n_full + t] = sv[j] * kLn2;
   }
   // online softmax step (as for a group)
   float mx = sv[0];
@@ -457,7 +590,7 @@ __device__ __forceinline__ void process_tail(const DecodeArgs& a, int64_t n_ctx,
   const bool grow = mx > m_run + kLazyMax;
   if (__any(grow)) {
     const float m_new = grow ? mx : m_run;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;  // as in softmax_step
     m_run = m_new;
     l_run *= alpha;
 #pragma unroll
@@ -467,7 +600,7 @@ __device__ __forceinline__ void process_tail(const DecodeArgs& a, int64_t n_ctx,
   float p[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    p[j] = __builtin_amdgcn_exp2f(sv[j] - m_run);  // 0 for the rows past n_ctx
+    p[j] = 8 * quad + j < own_len ? __builtin_amdgcn_exp2f(sv[j] - m_run) : 0.0f;
     l_run += p[j];
   }
 #pragma unroll 1
@@ -499,14 +632,17 @@ __device__ __forceinline__ void process_tail(const DecodeArgs& a, int64_t n_ctx,
   }
 }
 
-template <int D, int R, bool VQ2, bool NB>
+// J > 1: J groups per step share the matrix columns (2-bit values, g <= 16 / J; see process_block).
+template <int D, int R, bool VQ2, bool NB, int J>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_mfma_kernel(DecodeArgs a) {
+  static_assert(J == 1 || VQ2, "packed columns are built for 2-bit values");
   constexpr int NKT = D / 32, NCT = D / 16, NG = D / 32;
   constexpr int RU = R > 0 ? R : 1;
+  constexpr int SLOT = KSide<D, R, VQ2, NB>::BYTES;
   __shared__ float qs[kMaxGqa][D];            // scaled queries
   __shared__ float qu_s[kMaxGqa][RU];         // U^T q (scaled)
   __shared__ float inv_scale_s[kMaxGqa];      // 2^e undoing the per-head query scale
-  __shared__ u32x4 kslot[kWaves][KSide<D, R, VQ2, NB>::BYTES / 16];  // per-wave staging of a group
+  __shared__ u32x4 kslot[kWaves][J * SLOT / 16];  // per-wave staging of the groups of a step
   __shared__ float m_w[kWaves][kMaxGqa], l_w[kWaves][kMaxGqa];
   __shared__ float o_w[kWaves][kMaxGqa][D];
 
@@ -515,6 +651,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);  // uniform per wave: keeps group offsets scalar
   const int n = lane % 16, quad = lane / 16;
   const int g = a.gqa;
+  // column n of the matrix products: block jl (the step's group it follows) and head hd; columns
+  // past J * g are padding (their results are never merged)
+  const int jl = J > 1 ? n / g : 0, hd = J > 1 ? n % g : n;
   const int hq0 = h * g;
   const int64_t bh = (int64_t)b * a.hkv + h;
 
@@ -568,18 +707,41 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int rot = n_groups > 0 ? (int)((bh * 40503) % n_groups) : 0;
   auto group_at = [&](int j) { const int x = j + rot; return x >= n_groups ? x - n_groups : x; };
   const int j_begin = split * kWaves + wave;
+  // (contiguous caches: an empty resource over valid memory, so any load from it reads 0)
   const __amdgpu_buffer_rsrc_t table_row =
-      make_rsrc(a.map.block_table ? a.map.block_table + (int64_t)b * a.map.max_pages : nullptr,
+      make_rsrc(a.map.block_table ? (const void*)(a.map.block_table + (int64_t)b * a.map.max_pages)
+                                  : (const void*)a.kcode,
                 a.map.block_table ? a.map.max_pages * 4 : 0);
   auto page_at = [&](int j) { return j < n_groups ? request_page(a, table_row, group_at(j)) : 0; };
+  // J > 1: the page of a step's group requested unconditionally (index clamped into the row;
+  // n_groups >= 1 wherever it is called), so that the load into the page register never has to
+  // wait for the previous one (a register write of 0 on the other path would)
+  auto page_req = [&](int j) {
+    const int x = group_at(j);
+    const int off = __builtin_amdgcn_readfirstlane((x < n_groups ? x : n_groups - 1) * 4);
+    return (int)__builtin_amdgcn_raw_buffer_load_b32(table_row, 0, off, 0);
+  };
   int pa = 0, pb = 0;          // pages of the next groups loaded into ga / gb (paged caches)
   GroupRaw<D, R, VQ2, NB> ga, gb;  // ping-pong register sets: one group computed while the next loads
+  GroupRaw<D, R, VQ2, NB> gj[J];   // J > 1: the next step's groups, loaded while a step computes
+  int pj[J];                       // J > 1: their pages (paged caches), requested one step ahead
   auto first_loads = [&]() {
-    if (j_begin < n_groups) load_group<D, R, VQ2, NB>(ga, s, a, h, page_at(j_begin), lane, n, quad, group_at(j_begin));
-    if (j_begin + W < n_groups)
-      load_group<D, R, VQ2, NB>(gb, s, a, h, page_at(j_begin + W), lane, n, quad, group_at(j_begin + W));
-    pa = page_at(j_begin + 2 * W);
-    pb = page_at(j_begin + 3 * W);
+    if constexpr (J == 1) {
+      if (j_begin < n_groups)
+        load_group<D, R, VQ2, NB>(ga, s, a, h, page_at(j_begin), lane, n, quad, group_at(j_begin));
+      if (j_begin + W < n_groups)
+        load_group<D, R, VQ2, NB>(gb, s, a, h, page_at(j_begin + W), lane, n, quad, group_at(j_begin + W));
+      pa = page_at(j_begin + 2 * W);
+      pb = page_at(j_begin + 3 * W);
+    } else {
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int sl = j_begin + W * j;
+        if (sl < n_groups) load_group<D, R, VQ2, NB>(gj[j], s, a, h, page_at(sl), lane, n, quad, group_at(sl));
+      }
+#pragma unroll
+      for (int j = 0; j < J; ++j) pj[j] = page_at(j_begin + W * (J + j));
+    }
   };
   // the wave that takes the unfinished group requests its first groups after it (fewer live registers)
   const bool tail_wave = n_ctx % kGroup && split == 0 && wave == 0;
@@ -617,23 +779,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   for (int t = 0; t < NKT; ++t)
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float x = qs[n][(D / 4) * quad + 8 * t + j];
+      const float x = qs[hd][(D / 4) * quad + 8 * t + j];
       f.bq_hi[t][j] = f16_hi(x);
       f.bq_lo[t][j] = f16_lo(x);
     }
-  f.inv_scale = inv_scale_s[n];
+  f.inv_scale = inv_scale_s[hd];
   f.kappa = a.corr_scale;
   if constexpr (R == 32) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      f.bu_hi8[j] = f16_hi(qu_s[n][8 * quad + j]);
-      f.bu_lo8[j] = f16_lo(qu_s[n][8 * quad + j]);
+      f.bu_hi8[j] = f16_hi(qu_s[hd][8 * quad + j]);
+      f.bu_lo8[j] = f16_lo(qu_s[hd][8 * quad + j]);
     }
   } else if constexpr (R > 0) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int r = 4 * quad + j;
-      const float x = r < R ? qu_s[n][r] : 0.0f;
+      const float x = r < R ? qu_s[hd][r] : 0.0f;
       f.bu_hi4[j] = f16_hi(x);
       f.bu_lo4[j] = f16_lo(x);
     }
@@ -649,12 +811,42 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
   // ---- the unfinished last group (exact, from the tails), by one wave per stream
   if (tail_wave) {
-    process_tail<D>(a, n_ctx, bh, b, hq0, g, n, quad, qs, f.inv_scale, o_acc, z_acc, VQ2 ? NG : 0, m_run, l_run);
+    process_tail<D>(a, n_ctx, bh, b, hq0, g, n, hd, J == 1 || jl == 0, quad, qs, f.inv_scale, o_acc, z_acc,
+                    VQ2 ? NG : 0, m_run, l_run);
     first_loads();
   }
 
   // ---- this wave's groups
   uint8_t* slot = reinterpret_cast<uint8_t*>(kslot[wave]);
+  if constexpr (J > 1) {
+    // steps of J groups (the wave's group slots j_begin + W*k, k = k0 .. k0+J-1): stage the
+    // step's groups, request the next step's, compute this one from LDS
+    for (int k0 = 0; j_begin + W * k0 < n_groups; k0 += J) {
+      int nv = 0, gis[J];
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int sl = j_begin + W * (k0 + j);
+        nv = sl < n_groups ? j + 1 : nv;
+        gis[j] = group_at(sl < n_groups ? sl : j_begin + W * k0);
+      }
+      lds_wave_fence();
+#pragma unroll
+      for (int j = 0; j < J; ++j)
+        if (j < nv) stage_group<D, R, VQ2, NB>(gj[j], slot + j * SLOT, lane);
+      lds_wave_fence();
+      typename Bytes<D / 8>::T vcs[J];
+#pragma unroll
+      for (int j = 0; j < J; ++j) vcs[j] = gj[j].vc;
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int sl = j_begin + W * (k0 + J + j);
+        if (sl < n_groups) load_group<D, R, VQ2, NB>(gj[j], s, a, h, pj[j], lane, n, quad, group_at(sl));
+      }
+#pragma unroll
+      for (int j = 0; j < J; ++j) pj[j] = page_req(j_begin + W * (k0 + 2 * J + j));
+      process_block<D, R, NB, J>(vcs, gis, nv, f, slot, a, b, hq0, g, jl, hd, n, quad, o_acc, z_acc, m_run, l_run);
+    }
+  } else
   for (int j = j_begin; j < n_groups; j += 2 * W) {
     process_group<D, R, VQ2, NB>(ga, f, slot, a, group_at(j), b, hq0, g, lane, n, quad, o_acc, z_acc, m_run, l_run);
     if (j + W >= n_groups) break;
@@ -699,18 +891,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   __shared__ int last_s;
   for (int i = tid; i < g * D; i += kThreads) {
     const int hh = i / D, c = i % D;
+    // partials: every wave, and every block of columns of a packed layout (column jb*g + hh)
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, m_w[w][hh]);
+    for (int w = 0; w < kWaves; ++w)
+#pragma unroll
+      for (int jb = 0; jb < J; ++jb) M = fmaxf(M, m_w[w][jb * g + hh]);
     float L = 0.0f, O = 0.0f;
     if (M != -INFINITY) {
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        if (m_w[w][hh] == -INFINITY) continue;
-        const float fct = exp2f(m_w[w][hh] - M);
-        L = fmaf(l_w[w][hh], fct, L);
-        O = fmaf(o_w[w][hh][c], fct, O);
-      }
+      for (int w = 0; w < kWaves; ++w)
+#pragma unroll
+        for (int jb = 0; jb < J; ++jb) {
+          const int col = jb * g + hh;
+          if (m_w[w][col] == -INFINITY) continue;
+          const float fct = exp2f(m_w[w][col] - M);
+          L = fmaf(l_w[w][col], fct, L);
+          O = fmaf(o_w[w][col][c], fct, O);
+        }
     }
     const int64_t row = ((int64_t)b * a.hq + hq0 + hh) * a.n_splits + split;
     publish(a.ws_o + row * D + c, O);
@@ -774,18 +972,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   if (tid == 0) atomicExch(a.ws_count + bh, 0u);
 }
 
-template <int D, bool VQ2, bool NB>
-hipError_t launch_r(const DecodeArgs& a, hipStream_t s) {
+template <int D, bool VQ2, bool NB, int J>
+hipError_t launch_rj(const DecodeArgs& a, hipStream_t s) {
   dim3 grid((unsigned)a.n_splits, (unsigned)a.hkv, (unsigned)a.batch);
   switch (a.r) {
-    case 0: hipLaunchKernelGGL((decode_mfma_kernel<D, 0, VQ2, NB>), grid, dim3(kThreads), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((decode_mfma_kernel<D, 4, VQ2, NB>), grid, dim3(kThreads), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((decode_mfma_kernel<D, 8, VQ2, NB>), grid, dim3(kThreads), 0, s, a); break;
-    case 16: hipLaunchKernelGGL((decode_mfma_kernel<D, 16, VQ2, NB>), grid, dim3(kThreads), 0, s, a); break;
-    case 32: hipLaunchKernelGGL((decode_mfma_kernel<D, 32, VQ2, NB>), grid, dim3(kThreads), 0, s, a); break;
+    case 0: hipLaunchKernelGGL((decode_mfma_kernel<D, 0, VQ2, NB, J>), grid, dim3(kThreads), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((decode_mfma_kernel<D, 4, VQ2, NB, J>), grid, dim3(kThreads), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((decode_mfma_kernel<D, 8, VQ2, NB, J>), grid, dim3(kThreads), 0, s, a); break;
+    case 16: hipLaunchKernelGGL((decode_mfma_kernel<D, 16, VQ2, NB, J>), grid, dim3(kThreads), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((decode_mfma_kernel<D, 32, VQ2, NB, J>), grid, dim3(kThreads), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+// 2-bit values with few heads per KV head: J = 16 / g groups (at most 3) share the matrix columns.
+template <int D, bool VQ2, bool NB>
+hipError_t launch_r(const DecodeArgs& a, hipStream_t s) {
+  if constexpr (VQ2) {
+    const int j = a.pack_columns ? (a.gqa <= 5 ? 3 : a.gqa <= 8 ? 2 : 1) : 1;
+    if (j == 3) return launch_rj<D, true, NB, 3>(a, s);
+    if (j == 2) return launch_rj<D, true, NB, 2>(a, s);
+  }
+  return launch_rj<D, VQ2, NB, 1>(a, s);
 }
 
 }  // namespace

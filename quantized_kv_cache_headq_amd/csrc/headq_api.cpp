@@ -173,6 +173,16 @@ bool decode_uses_mfma(const headq_config* c) {
   return !force_valu && (c->value_mode == HEADQ_V_Q2 || c->value_dtype == HEADQ_BF16);
 }
 
+// With 2-bit values and g <= 8 heads per KV head the matrix-core kernel lets 16 / g groups share
+// the 16 matrix columns; HEADQ_DECODE_PACK=0 keeps one group per product (the measured comparison).
+bool decode_packs_columns() {
+  static const bool off = [] {
+    const char* s = std::getenv("HEADQ_DECODE_PACK");
+    return s && std::strcmp(s, "0") == 0;
+  }();
+  return !off;
+}
+
 // Token splits per (b, h) stream. The matrix-core kernel aims at one wave per SIMD (1024 waves
 // over the 256 CUs: measured faster than two, which contend for the same issue slots and memory
 // queues), the vector kernel at two; every chunk (the groups one wave walks) stays at least 4
@@ -226,6 +236,7 @@ extern "C" headq_status headq_decode_attn(const headq_config* cfg, const headq_c
   headq::DecodeArgs a{};
   a.d = cfg->head_dim;
   a.key_nib = cfg->base_bits != 2;
+  a.pack_columns = decode_packs_columns();
   a.r = cfg->rank;
   a.hq = cfg->n_q_heads;
   a.hkv = cfg->n_kv_heads;

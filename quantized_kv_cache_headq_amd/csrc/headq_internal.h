@@ -90,6 +90,7 @@ struct DecodeArgs {
   int use_mfma;                // matrix-core kernel (dense bf16 or 2-bit values)
   int query_bf16, value_bf16, value_mode, out_bf16;
   int key_nib;                 // 3- or 4-bit base codes (one per nibble)
+  int pack_columns;            // 2-bit values, g <= 8: several groups share the matrix columns
   float corr_scale;
   const void* q;
   const uint8_t* kcode;

@@ -33,15 +33,16 @@ def _oracle(w, U, K, V, cap, pieces):
     return oc
 
 
-def _decode_case(w, B, pieces, cap, out_bf16=False):
+def _decode_case(w, B, pieces, cap, out_bf16=False, n_splits=0):
     T = sum(n for _, n in pieces)
-    say("bits", w.name, f"bits={w.base_bits} B={B} T={T} d={w.head_dim} r={w.rank} v={w.value_mode}/{w.value_dtype}")
+    say("decode", w.name, f"bits={w.base_bits} B={B} T={T} d={w.head_dim} r={w.rank} g={w.gqa}",
+        f"v={w.value_mode}/{w.value_dtype} splits={n_splits}")
     U = orc.calibrate(synth.calibration_queries(w, n_cal=128), w.n_kv_heads, w.rank)[0] if w.rank else None
     dc, K, V = gpu_cache(w, U, B, T, cap, pieces=pieces)
     oc = _oracle(w, U, K, V, cap, pieces)
     compare_cache(dc, oc)
     q = synth.decode_queries(w, position=T, batch=B)
-    lg, out = decode_gpu(dc, w, q, T, out_bf16=out_bf16)
+    lg, out = decode_gpu(dc, w, q, T, out_bf16=out_bf16, n_splits=n_splits)
     ref_l, ref_o = orc.decode(oc, q, U, T, 1.0, VMODE[w.value_mode], VDT[w.value_dtype])
     check_logits(lg, ref_l)
     check_out(out, ref_o, out_bf16)

@@ -155,3 +155,17 @@ def test_workspace_counters_return_to_zero_and_reuse():
         torch.cuda.synchronize()
         check_out(out.cpu().numpy(), ref, False)
         assert int(ws[:64].abs().sum().item()) == 0, f"counters not reset after n_splits={s}"
+
+
+@pytest.mark.parametrize("g,d,T,splits", [(7, 128, 213, 2), (8, 64, 40, 0), (3, 128, 352, 3), (2, 128, 1000, 0),
+                                          (5, 128, 45, 1), (6, 64, 300, 2), (4, 128, 96, 3)])
+def test_packed_columns_two_bit_values(g, d, T, splits):
+    """2-bit values with g <= 8: 16 // g groups (at most 3) share the matrix columns. Ragged ends
+    (steps with fewer groups than columns blocks, waves without groups), a dense tail, padding
+    columns, splits."""
+    base = W["qwen14b_fullkv"] if d == 128 else synth.scaled(W["tinyllama_decode"], value_mode="q2")
+    w = synth.scaled(base, n_q_heads=2 * g, n_kv_heads=2)
+    from .test_gpu_bits import _decode_case
+    n_full = T // 32 * 32
+    pieces = [p for p in [(0, n_full), (n_full, T - n_full)] if p[1]]
+    _decode_case(w, 2, pieces, (T + 31) // 32 * 32, out_bf16=g % 2 == 0, n_splits=splits)
