@@ -304,6 +304,90 @@ int orc_quantize_values(int d, int bits, int64_t T, const float* v, uint8_t* cod
 }
 
 /* ------------------------------------------------------------------------------------------ */
+/* A^2 value policy ([TS] §2.2: values are read through the weighted sum, and their error is
+ * measured by the A^2 surrogate sum_j p_j^2 |v_hat_j - v_j|^2; §5: the full-KV composition pairs
+ * HeadQ keys with an A^2-weighted value policy). The pages define the surrogate, not the policy.
+ * Reading: every token keeps its 2-bit value codes; per 32-token group, P of them also keep a
+ * correction delta_j = v_j - v_hat_j in bfloat16 (the decoded value is then v_hat_j + delta_j):
+ * the P tokens with the largest estimated reduction of the surrogate, w_j * e_j, where
+ *   e_j = |v_j - v_hat_j|^2, v_hat = fma(code, s, z) per channel, summed by one f32 fma chain
+ *         over channels 0..d-1 from +0;
+ *   w_j = 2^n_j, n_j = clamp(rint(c2 * (a_h . k_j)), -64, 64): a power-of-two estimate of
+ *         exp(2 a_h.k_j / sqrt(d)), to which E[p_j^2] is proportional within a group at first
+ *         order in the query, a_h the mean post-RoPE calibration query of the KV head, a_h . k_j
+ *         one f32 fma chain over channels 0..d-1 from +0, c2 = 2 log2(e) / sqrt(d) rounded to f32;
+ *   w_j * e_j compared exactly (in double); ties go to the lower token index.
+ * The chosen tokens fill the P slots in ascending token order. */
+float orc_policy_scale(int d) { return (float)(2.0 * 1.4426950408889634 / sqrt((double)d)); }
+
+/* Mean calibration query per KV head (the direction a_h above): f64 sums over the g query heads
+ * of the KV head (in head order) and their n_cal queries (in order), divided by g * n_cal, rounded
+ * to f32. q_cal: f32 [Hq][n_cal][d]; a: f32 [Hkv][d]. */
+int orc_mean_query(int d, int hq, int hkv, int64_t n_cal, const float* q_cal, float* a) {
+  if (d <= 0 || hq <= 0 || hkv <= 0 || hq % hkv || n_cal <= 0 || !q_cal || !a) return -1;
+  const int g = hq / hkv;
+  for (int h = 0; h < hkv; ++h)
+    for (int c = 0; c < d; ++c) {
+      double acc = 0.0;
+      for (int hh = h * g; hh < (h + 1) * g; ++hh)
+        for (int64_t n = 0; n < n_cal; ++n) acc += (double)q_cal[((int64_t)hh * n_cal + n) * d + c];
+      a[(int64_t)h * d + c] = (float)(acc / ((double)g * (double)n_cal));
+    }
+  return 0;
+}
+
+/* The policy over whole groups of one stream. k, v: f32 [T][d] (keys and values as written);
+ * a: f32 [d]; codes/scale/zero: the 2-bit value quantizer's output for v. Writes idx u8 [T/32][4]
+ * (slot i < P: token index in the group; the other bytes 0) and delta bf16 bits [T/32][P][d];
+ * prio (optional, f64 [T]): w_j * e_j. */
+int orc_value_policy(int d, int P, int64_t T, const float* k, const float* v, const float* a,
+                     const uint8_t* codes, const uint16_t* scale, const uint16_t* zero, uint8_t* idx,
+                     uint16_t* delta, double* prio) {
+  if (d <= 0 || d % GROUP || P < 1 || P > 4 || T <= 0 || T % GROUP || !k || !v || !a || !codes || !scale ||
+      !zero || !idx || !delta)
+    return -1;
+  const int ng = d / GROUP;
+  const float c2 = orc_policy_scale(d);
+  double pr[GROUP];
+  for (int64_t g0 = 0; g0 < T; g0 += GROUP) {
+    const int64_t gi = g0 / GROUP;
+    for (int t = 0; t < GROUP; ++t) {
+      const int64_t row = g0 + t;
+      float dot = 0.0f, e = 0.0f;
+      for (int c = 0; c < d; ++c) dot = fmaf(a[c], k[row * d + c], dot);
+      for (int c = 0; c < d; ++c) {
+        const float s = orc_f16_to_f32(scale[row * ng + c / GROUP]);
+        const float z = orc_f16_to_f32(zero[row * ng + c / GROUP]);
+        const float diff = v[row * d + c] - fmaf((float)codes[row * d + c], s, z);
+        e = fmaf(diff, diff, e);
+      }
+      float nf = nearbyintf(dot * c2);
+      if (nf < -64.0f) nf = -64.0f;
+      if (nf > 64.0f) nf = 64.0f;
+      pr[t] = ldexp((double)e, (int)nf);
+      if (prio) prio[row] = pr[t];
+    }
+    int slot = 0;
+    for (int i = 0; i < 4; ++i) idx[gi * 4 + i] = 0;
+    for (int t = 0; t < GROUP; ++t) {
+      int rank = 0;
+      for (int u = 0; u < GROUP; ++u)
+        if (pr[u] > pr[t] || (pr[u] == pr[t] && u < t)) ++rank;
+      if (rank >= P) continue;
+      idx[gi * 4 + slot] = (uint8_t)t;
+      const int64_t row = g0 + t;
+      for (int c = 0; c < d; ++c) {
+        const float s = orc_f16_to_f32(scale[row * ng + c / GROUP]);
+        const float z = orc_f16_to_f32(zero[row * ng + c / GROUP]);
+        delta[(gi * P + slot) * d + c] = orc_f32_to_bf16(v[row * d + c] - fmaf((float)codes[row * d + c], s, z));
+      }
+      ++slot;
+    }
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------------------------ */
 /* Packing into the cache format (byte layouts are this repository's convention). */
 
 /* Bit position of channel 16m + j inside the 32-bit little-endian word m of a token's key codes:
@@ -427,8 +511,12 @@ static double k_hat(const uint8_t* kcode_t, const uint16_t* kmeta_g, int d, int 
   return (double)code * s + z;
 }
 
+/* The value of token t, channel c of one stream: dense as stored, or 2-bit code * s + z plus the
+ * policy's correction when the token holds one of its group's n_prot slots (vpidx u8 [G][4],
+ * vprot bf16 bits [G][n_prot][d] of the stream). */
 static double v_hat(int value_mode, int value_dtype, const void* vdense, const uint8_t* vcode,
-                    const uint16_t* vmeta, int d, int64_t t, int c) {
+                    const uint16_t* vmeta, int d, int64_t t, int c, int n_prot, const uint8_t* vpidx,
+                    const uint16_t* vprot) {
   int64_t g = t / GROUP, tt = t % GROUP;
   if (value_mode == 0) {
     int64_t idx = (g * d + c) * GROUP + tt;
@@ -439,7 +527,10 @@ static double v_hat(int value_mode, int value_dtype, const void* vdense, const u
   unsigned code = (vcode[g * d * 8 + vcode_byte(d, c, (int)tt)] >> vcode_bit((int)tt)) & 3u;
   double s = orc_f16_to_f32(vmeta[((g * 2 + 0) * ng + c / GROUP) * GROUP + tt]);
   double z = orc_f16_to_f32(vmeta[((g * 2 + 1) * ng + c / GROUP) * GROUP + tt]);
-  return (double)code * s + z;
+  double x = (double)code * s + z;
+  for (int i = 0; i < n_prot; ++i)
+    if (vpidx[g * 4 + i] == tt) x += orc_bf16_to_f32(vprot[(g * n_prot + i) * d + c]);
+  return x;
 }
 
 /* An element of a dense tail row (f32, or bfloat16 bits when dtype == 1). */
@@ -452,10 +543,12 @@ int orc_decode(int d, int hq, int hkv, int r, int value_mode, int value_dtype, i
                int64_t n_ctx, const uint8_t* kcode, const uint16_t* kmeta, const uint8_t* scode,
                const uint16_t* ssc, const void* vdense, const uint8_t* vcode, const uint16_t* vmeta,
                int key_dtype, const void* ktail, const void* vtail, const float* U, const float* q, double kappa,
-               int b_begin, int b_end, double* logits, double* out, int base_bits) {
+               int b_begin, int b_end, double* logits, double* out, int base_bits, int n_prot,
+               const uint8_t* vpidx, const uint16_t* vprot) {
   if (d <= 0 || d % 4 || hq <= 0 || hkv <= 0 || hq % hkv || r < 0 || r % 2 || cap % GROUP || n_ctx <= 0 ||
       n_ctx > cap || b_begin < 0 || b_end > B || b_begin > b_end || !kcode || !kmeta || !q || !out ||
-      base_bits < 2 || base_bits > 4)
+      base_bits < 2 || base_bits > 4 || n_prot < 0 || n_prot > 4 ||
+      (n_prot && (value_mode != 1 || !vpidx || !vprot)))
     return -1;
   const int row_bytes = base_bits == 2 ? d / 4 : d / 2;  /* packed key codes per token */
   /* tokens past the last whole group are the stream's dense tail: exact keys and values */
@@ -511,6 +604,8 @@ int orc_decode(int d, int hq, int hkv, int r, int value_mode, int value_dtype, i
       const void* vd = vdense ? (const void*)((const uint8_t*)vdense + bh * cap * d * vb) : NULL;
       const uint8_t* vc = vcode ? vcode + bh * (cap / GROUP) * d * 8 : NULL;
       const uint16_t* vm = vmeta ? vmeta + bh * (cap / GROUP) * 2 * d : NULL;
+      const uint8_t* pi = n_prot ? vpidx + bh * (cap / GROUP) * 4 : NULL;
+      const uint16_t* pv = n_prot ? vprot + bh * (cap / GROUP) * n_prot * d : NULL;
       double l = 0.0;
       for (int64_t j = 0; j < n_ctx; ++j) l += exp(s[j] - smax);
       for (int c = 0; c < d; ++c) o[c] = 0.0;
@@ -519,7 +614,8 @@ int orc_decode(int d, int hq, int hkv, int r, int value_mode, int value_dtype, i
         if (j >= n_full)
           for (int c = 0; c < d; ++c) o[c] += p * tail_at(vtail, value_dtype, (bh * GROUP + j % GROUP) * d + c);
         else
-          for (int c = 0; c < d; ++c) o[c] += p * v_hat(value_mode, value_dtype, vd, vc, vm, d, j, c);
+          for (int c = 0; c < d; ++c)
+            o[c] += p * v_hat(value_mode, value_dtype, vd, vc, vm, d, j, c, n_prot, pi, pv);
       }
       for (int c = 0; c < d; ++c) out[((int64_t)b * hq + a) * d + c] = o[c];
       if (logits)
@@ -535,8 +631,10 @@ int orc_decode(int d, int hq, int hkv, int r, int value_mode, int value_dtype, i
  * past the last whole group from the dense tail. out: f64 [n_ctx][d]. */
 int orc_value_rows(int d, int value_mode, int value_dtype, int hkv, int64_t cap, int64_t n_ctx,
                    const void* vdense, const uint8_t* vcode, const uint16_t* vmeta, const void* vtail, int b,
-                   int h, double* out) {
-  if (d <= 0 || cap % GROUP || n_ctx < 0 || n_ctx > cap || b < 0 || h < 0 || h >= hkv || !out) return -1;
+                   int h, double* out, int n_prot, const uint8_t* vpidx, const uint16_t* vprot) {
+  if (d <= 0 || cap % GROUP || n_ctx < 0 || n_ctx > cap || b < 0 || h < 0 || h >= hkv || !out || n_prot < 0 ||
+      n_prot > 4 || (n_prot && (value_mode != 1 || !vpidx || !vprot)))
+    return -1;
   const int64_t n_full = n_ctx / GROUP * GROUP;
   if (n_full < n_ctx && !vtail) return -1;
   if (value_mode == 0 && !vdense) return -1;
@@ -546,10 +644,12 @@ int orc_value_rows(int d, int value_mode, int value_dtype, int hkv, int64_t cap,
   const void* vd = vdense ? (const void*)((const uint8_t*)vdense + bh * cap * d * vb) : NULL;
   const uint8_t* vc = vcode ? vcode + bh * (cap / GROUP) * d * 8 : NULL;
   const uint16_t* vm = vmeta ? vmeta + bh * (cap / GROUP) * 2 * d : NULL;
+  const uint8_t* pi = n_prot ? vpidx + bh * (cap / GROUP) * 4 : NULL;
+  const uint16_t* pv = n_prot ? vprot + bh * (cap / GROUP) * n_prot * d : NULL;
   for (int64_t j = 0; j < n_ctx; ++j)
     for (int c = 0; c < d; ++c)
       out[j * d + c] = j >= n_full ? tail_at(vtail, value_dtype, (bh * GROUP + j % GROUP) * d + c)
-                                   : v_hat(value_mode, value_dtype, vd, vc, vm, d, j, c);
+                                   : v_hat(value_mode, value_dtype, vd, vc, vm, d, j, c, n_prot, pi, pv);
   return 0;
 }
 

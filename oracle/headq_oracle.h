@@ -58,6 +58,15 @@ int orc_encode_keys(int d, int r, int bits, int side_bits, int64_t T, const floa
 int orc_quantize_values(int d, int bits, int64_t T, const float* v, uint8_t* codes, uint16_t* scale,
                         uint16_t* zero);
 
+/* A^2 value policy (definition in headq_oracle.c): c2 = 2 log2(e) / sqrt(d) in f32; the mean
+ * calibration query per KV head; the per-group choice of P corrected tokens and their bfloat16
+ * corrections. */
+float orc_policy_scale(int d);
+int orc_mean_query(int d, int hq, int hkv, int64_t n_cal, const float* q_cal, float* a);
+int orc_value_policy(int d, int P, int64_t T, const float* k, const float* v, const float* a,
+                     const uint8_t* codes, const uint16_t* scale, const uint16_t* zero, uint8_t* idx,
+                     uint16_t* delta, double* prio);
+
 /* Packing into the cache format (one stream; offsets for (b, h) are the caller's).
  *   kcode [T][d/4] (d % 16 == 0): d/16 little-endian 32-bit words per token; channel 16m + j with
  *         j = 8q + 2b + e lies in word m, byte b, bits 4e + 2q (so masking a word with 0x33333333
@@ -89,19 +98,22 @@ int orc_pack_vmeta(int d, int64_t T, const uint16_t* scale, const uint16_t* zero
  * last whole group (n_ctx % 32 of them) come from the dense tails ktail / vtail [B][hkv][32][d]
  * (row t % 32; f32, or bfloat16 bits when the dtype is 1) with exact keys and values: no base
  * code, no side code. The tails may be NULL when n_ctx is a multiple of 32. base_bits (2, 3 or 4)
- * selects the key-code packing: 2-bit words, or one code per nibble for 3 and 4 bits. */
+ * selects the key-code packing: 2-bit words, or one code per nibble for 3 and 4 bits. n_prot > 0
+ * (2-bit values only): the A^2 value policy's corrections, vpidx u8 [B][hkv][cap/32][4] and vprot
+ * bf16 bits [B][hkv][cap/32][n_prot][d], added to the values of the tokens they name. */
 int orc_decode(int d, int hq, int hkv, int r, int value_mode, int value_dtype, int B, int64_t cap,
                int64_t n_ctx, const uint8_t* kcode, const uint16_t* kmeta, const uint8_t* scode,
                const uint16_t* ssc, const void* vdense, const uint8_t* vcode, const uint16_t* vmeta,
                int key_dtype, const void* ktail, const void* vtail, const float* U, const float* q, double kappa,
-               int b_begin, int b_end, double* logits, double* out, int base_bits);
+               int b_begin, int b_end, double* logits, double* out, int base_bits, int n_prot,
+               const uint8_t* vpidx, const uint16_t* vprot);
 
 /* Value rows of stream (b, h) as the cache holds them, in fp64: out [n_ctx][d] (dense values as
- * stored, 2-bit values as code * s + z, tokens past the last whole group from vtail). Cache
- * buffers as for orc_decode. */
+ * stored, 2-bit values as code * s + z plus the policy's corrections, tokens past the last whole
+ * group from vtail). Cache buffers as for orc_decode. */
 int orc_value_rows(int d, int value_mode, int value_dtype, int hkv, int64_t cap, int64_t n_ctx,
                    const void* vdense, const uint8_t* vcode, const uint16_t* vmeta, const void* vtail, int b,
-                   int h, double* out);
+                   int h, double* out, int n_prot, const uint8_t* vpidx, const uint16_t* vprot);
 
 #ifdef __cplusplus
 }

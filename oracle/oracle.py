@@ -59,8 +59,13 @@ def lib():
         L.orc_pack_vdense.argtypes = [I, I64, I, P, P]
         L.orc_pack_vcode.argtypes = [I, I64, P, P]
         L.orc_pack_vmeta.argtypes = [I, I64, P, P, P]
-        L.orc_decode.argtypes = [I, I, I, I, I, I, I, I64, I64, P, P, P, P, P, P, P, I, P, P, P, P, D, I, I, P, P, I]
-        L.orc_value_rows.argtypes = [I, I, I, I, I64, I64, P, P, P, P, I, I, P]
+        L.orc_decode.argtypes = [I, I, I, I, I, I, I, I64, I64, P, P, P, P, P, P, P, I, P, P, P, P, D, I, I, P, P, I,
+                                 I, P, P]
+        L.orc_value_rows.argtypes = [I, I, I, I, I64, I64, P, P, P, P, I, I, P, I, P, P]
+        L.orc_policy_scale.restype = ctypes.c_float
+        L.orc_policy_scale.argtypes = [I]
+        L.orc_mean_query.argtypes = [I, I, I, I64, P, P]
+        L.orc_value_policy.argtypes = [I, I, I64, P, P, P, P, P, P, P, P, P]
         _lib = L
     return _lib
 
@@ -136,6 +141,33 @@ def encode_keys(k, U, bits: int = 2, side_bits: int = 4):
     return out
 
 
+def mean_query(q_cal, n_kv_heads: int):
+    """Mean calibration query per KV head (the A^2 value policy's direction): f32 [Hq][n_cal][d]
+    -> f32 [Hkv][d]."""
+    q = np.ascontiguousarray(q_cal, dtype=np.float32)
+    hq, n_cal, d = q.shape
+    a = np.zeros((n_kv_heads, d), np.float32)
+    _check(lib().orc_mean_query(d, hq, n_kv_heads, n_cal, _p(q), _p(a)), "mean_query")
+    return a
+
+
+def value_policy(k, v, a_h, n_prot: int):
+    """The A^2 value policy over whole groups of one stream: k, v f32 [T][d], a_h f32 [d]. Returns
+    dict(idx u8 [T/32][4], delta bf16 bits [T/32][P][d], prio f64 [T], and the 2-bit value
+    quantizer's codes/scale/zero)."""
+    k = np.ascontiguousarray(k, np.float32)
+    v = np.ascontiguousarray(v, np.float32)
+    a_h = np.ascontiguousarray(a_h, np.float32)
+    T, d = v.shape
+    vq = quantize_values(v, 2)
+    idx = np.zeros((T // GROUP, 4), np.uint8)
+    delta = np.zeros((T // GROUP, n_prot, d), np.uint16)
+    prio = np.zeros(T, np.float64)
+    _check(lib().orc_value_policy(d, n_prot, T, _p(k), _p(v), _p(a_h), _p(vq["codes"]), _p(vq["scale"]),
+                                  _p(vq["zero"]), _p(idx), _p(delta), _p(prio)), "value_policy")
+    return dict(idx=idx, delta=delta, prio=prio, **vq)
+
+
 def quantize_values(v, bits: int = 2):
     v = np.ascontiguousarray(v, dtype=np.float32)
     T, d = v.shape
@@ -146,11 +178,13 @@ def quantize_values(v, bits: int = 2):
     return dict(codes=codes, scale=scale, zero=zero)
 
 
-def empty_cache(B, Hkv, cap, d, r, value_mode, value_dtype, key_dtype=None, base_bits=2):
+def empty_cache(B, Hkv, cap, d, r, value_mode, value_dtype, key_dtype=None, base_bits=2, value_protect=0):
     """Zero-filled buffers of the cache format (numpy, host). With key_dtype given, the dense tails
     of the unfinished last group are included: ktail / vtail [B][Hkv][32][d] in the key / value
     dtype (f32, or bfloat16 bit patterns). base_bits 2 packs four key codes per byte; 3 and 4 one
-    code per nibble (kcode rows of d/2 bytes)."""
+    code per nibble (kcode rows of d/2 bytes). value_protect P > 0 (2-bit values): the A^2 value
+    policy's vpidx u8 [B][Hkv][cap/32][4] and vprot bf16 bits [B][Hkv][cap/32][P][d]; write_stream
+    then needs the direction a_h of each head."""
     c = dict(
         kcode=np.zeros((B, Hkv, cap, d // 4 if base_bits == 2 else d // 2), np.uint8),
         kmeta=np.zeros((B, Hkv, cap // GROUP, 2, d), np.uint16),
@@ -163,6 +197,9 @@ def empty_cache(B, Hkv, cap, d, r, value_mode, value_dtype, key_dtype=None, base
     else:
         c["vcode"] = np.zeros((B, Hkv, cap // GROUP, d * 8), np.uint8)
         c["vmeta"] = np.zeros((B, Hkv, cap // GROUP, 2, d // GROUP, GROUP), np.uint16)
+        if value_protect:
+            c["vpidx"] = np.zeros((B, Hkv, cap // GROUP, 4), np.uint8)
+            c["vprot"] = np.zeros((B, Hkv, cap // GROUP, value_protect, d), np.uint16)
     if key_dtype is not None:
         c["ktail"] = np.zeros((B, Hkv, GROUP, d), np.float32 if key_dtype == 0 else np.uint16)
         c["vtail"] = np.zeros((B, Hkv, GROUP, d), np.float32 if value_dtype == 0 else np.uint16)
@@ -184,7 +221,7 @@ def _from_tail(rows, as_bits):
     return rows.copy() if as_bits else bf16_bits_to_f32(rows)
 
 
-def write_stream(cache, b, h, start, k, v, U_h, value_mode, value_dtype, bits=2, side_bits=4):
+def write_stream(cache, b, h, start, k, v, U_h, value_mode, value_dtype, bits=2, side_bits=4, a_h=None):
     """Append tokens [start, start + n) of one (b, h) stream (the cache write of the summary's §3
     step 2, one token at a time or in any run). Every group that is whole once these tokens are in
     is encoded; the tokens of an unfinished last group are kept exactly in the dense tails. Tokens
@@ -192,10 +229,11 @@ def write_stream(cache, b, h, start, k, v, U_h, value_mode, value_dtype, bits=2,
 
     k: f32 [n][d] keys (exact widening of the stored key dtype)
     v: [n][d] values (f32 array for dtype 0, bf16 bit patterns uint16 for dtype 1, f32 for 2-bit)
+    a_h: f32 [d], the A^2 value policy's direction (caches with vprot)
     Returns the unpacked encode result of the whole groups (None if there are none)."""
     n, d = k.shape
     if start % GROUP == 0 and n % GROUP == 0:
-        return _write_groups(cache, b, h, start, k, v, U_h, value_mode, value_dtype, bits, side_bits)
+        return _write_groups(cache, b, h, start, k, v, U_h, value_mode, value_dtype, bits, side_bits, a_h)
     g0 = start // GROUP
     head = start - g0 * GROUP
     kt, vt = cache["ktail"][b, h], cache["vtail"][b, h]
@@ -209,7 +247,7 @@ def write_stream(cache, b, h, start, k, v, U_h, value_mode, value_dtype, bits=2,
     if n_whole > 0:
         m = n_whole * GROUP
         enc = _write_groups(cache, b, h, g0 * GROUP, k_all[:m], None if v_all is None else v_all[:m], U_h,
-                            value_mode, value_dtype, bits, side_bits)
+                            value_mode, value_dtype, bits, side_bits, a_h)
     rest = len(k_all) - n_whole * GROUP
     if rest:
         kt[:rest] = _to_tail(k_all[n_whole * GROUP:], kt)
@@ -218,7 +256,7 @@ def write_stream(cache, b, h, start, k, v, U_h, value_mode, value_dtype, bits=2,
     return enc
 
 
-def _write_groups(cache, b, h, start, k, v, U_h, value_mode, value_dtype, bits, side_bits):
+def _write_groups(cache, b, h, start, k, v, U_h, value_mode, value_dtype, bits, side_bits, a_h=None):
     """Encode whole groups (start and n multiples of 32) into the packed arrays."""
     n, d = k.shape
     r = 0 if U_h is None else U_h.shape[1]
@@ -255,6 +293,12 @@ def _write_groups(cache, b, h, start, k, v, U_h, value_mode, value_dtype, bits, 
             vm = np.zeros((n // GROUP, 2, d // GROUP, GROUP), np.uint16)
             _check(L.orc_pack_vmeta(d, n, _p(vq["scale"]), _p(vq["zero"]), _p(vm)), "pack_vmeta")
             cache["vmeta"][b, h, g0:g1] = vm
+            if "vprot" in cache:
+                if a_h is None:
+                    raise ValueError("a cache with the A^2 value policy needs the direction a_h")
+                pol = value_policy(k, v, a_h, cache["vprot"].shape[3])
+                cache["vpidx"][b, h, g0:g1] = pol["idx"]
+                cache["vprot"][b, h, g0:g1] = pol["delta"]
     return enc
 
 
@@ -288,11 +332,12 @@ def decode(cache, q, U, n_ctx, kappa=1.0, value_mode=0, value_dtype=1, b_range=N
     kt = arrs.get("ktail")
     key_dtype = 0 if kt is None or kt.dtype == np.float32 else 1
     layout_bits = 2 if kcode.shape[3] * 4 == d else 4  # packing only: the levels do not enter k_hat
+    n_prot = arrs["vprot"].shape[3] if "vprot" in arrs else 0
     _check(lib().orc_decode(d, Hq, Hkv, r, value_mode, value_dtype, B, cap, n_ctx, _p(arrs["kcode"]),
                             _p(arrs["kmeta"]), _p(arrs["scode"]) if r else None, _p(arrs["ssc"]) if r else None,
                             _p(arrs.get("v")), _p(arrs.get("vcode")), _p(arrs.get("vmeta")), key_dtype, _p(kt),
                             _p(arrs.get("vtail")), _p(Uc), _p(q), float(kappa), b0, b1, _p(logits), _p(out),
-                            layout_bits),
+                            layout_bits, n_prot, _p(arrs.get("vpidx")), _p(arrs.get("vprot"))),
            "decode")
     return logits, out
 
@@ -304,8 +349,10 @@ def value_rows(cache, b, h, n_ctx, value_mode=0, value_dtype=1):
     B, Hkv, cap, _ = arrs["kcode"].shape
     d = arrs["kmeta"].shape[-1]
     out = np.zeros((n_ctx, d), np.float64)
+    n_prot = arrs["vprot"].shape[3] if "vprot" in arrs else 0
     _check(lib().orc_value_rows(d, value_mode, value_dtype, Hkv, cap, n_ctx, _p(arrs.get("v")), _p(arrs.get("vcode")),
-                                _p(arrs.get("vmeta")), _p(arrs.get("vtail")), b, h, _p(out)), "value_rows")
+                                _p(arrs.get("vmeta")), _p(arrs.get("vtail")), b, h, _p(out), n_prot,
+                                _p(arrs.get("vpidx")), _p(arrs.get("vprot"))), "value_rows")
     return out
 
 
