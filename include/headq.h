@@ -53,10 +53,15 @@
  *                                        row 0 = step, row 1 = zero, token index fastest
  *   ktail  key_dtype   [B][Hkv][G][d]    tokens of the unfinished last group (row t % 32), exact
  *   vtail  value_dtype [B][Hkv][G][d]    their values, exact (also in 2-bit mode)
+ *   vpidx  u32  [B][Hkv][cap/G]          (value_protect = P > 0) byte i < P: the index in its group
+ *                                        of the token in correction slot i (ascending); others 0
+ *   vprot  bf16 [B][Hkv][cap/G][P][d]    (value_protect > 0) slot i: v - v_hat of that token, so
+ *                                        that the token's value reads v_hat + correction
  * Paged caches (block_table != NULL): every array above except U and the tails is instead a pool
  * of n_pages pages, the [B][Hkv][cap/G] group index replaced by [n_pages][Hkv]: the group g of
  * batch row b lives in page block_table[b * max_pages + g] (one page = one 32-token group of all
- * KV heads; e.g. kcode [n_pages][Hkv][G][d/4], v [n_pages][Hkv][d][G]); `capacity` is then the
+ * KV heads; e.g. kcode [n_pages][Hkv][G][d/4], v [n_pages][Hkv][d][G], vpidx [n_pages][Hkv]);
+ * `capacity` is then the
  * per-row logical capacity, at most 32 * max_pages. Pages are assigned by the caller; entries
  * outside [0, n_pages) are clamped by the kernels (to stay inside the pools).
  *   U      f32  [Hkv][d][r]              the side basis (device copy of headq_calibrate's output)
@@ -106,6 +111,9 @@ typedef struct headq_config {
                           the dense value store */
   int32_t value_mode;  /* HEADQ_V_DENSE or HEADQ_V_Q2 (2-bit values, d = 128 or 64) */
   int32_t query_dtype; /* HEADQ_F32 or HEADQ_BF16: dtype of decode queries */
+  int32_t value_protect; /* A^2 value policy: P tokens of every 32-token group that keep a bfloat16
+                            correction on top of their 2-bit value codes; 0 (off), 1 or 2; P > 0
+                            needs HEADQ_V_Q2 and base_bits 2 (see headq_calibrate_mean) */
 } headq_config;
 
 typedef struct headq_cache { /* device pointers, layouts in the header comment above */
@@ -122,6 +130,10 @@ typedef struct headq_cache { /* device pointers, layouts in the header comment a
   const int32_t* block_table; /* device int32 [B][max_pages]: paged cache, or NULL (contiguous) */
   int64_t max_pages;          /* pages per batch row in block_table */
   int64_t n_pages;            /* pages in each pool */
+  const float* vdir;          /* value_protect > 0: [Hkv][d], the policy's direction a_h
+                                 (device copy of headq_calibrate_mean's output) */
+  uint32_t* vpidx;            /* value_protect > 0: the policy's token indices per group */
+  uint16_t* vprot;            /* value_protect > 0: the policy's bfloat16 corrections */
 } headq_cache;
 
 /*
@@ -141,6 +153,25 @@ headq_status headq_calibrate(const headq_config* cfg, const float* q_cal, int64_
                              double* eig);
 
 /*
+ * headq_calibrate_mean — the direction of the A^2 value policy (host only, synchronous).
+ * Summary §2.2 measures value error by the A^2 surrogate sum_j p_j^2 |v_hat_j - v_j|^2 and §5
+ * pairs HeadQ keys with an A^2-weighted value policy; the pages do not define the policy. This
+ * library's reading (value_protect = P > 0, applied by headq_cache_append): per 32-token group the
+ * P tokens of largest w_j * e_j keep a bfloat16 correction v_j - v_hat_j, where
+ *   e_j = sum_c (v_jc - fma(code, s, z))^2, one f32 fma chain over c = 0..d-1 from +0,
+ *   w_j = 2^n_j, n_j = clamp(rint(c2 * (a_h . k_j)), -64, 64), a_h . k_j one f32 fma chain over
+ *         c = 0..d-1 from +0, c2 = f32(2 log2(e) / sqrt(d)): a power-of-two estimate of
+ *         exp(2 a_h.k_j / sqrt(d)), to which E[p_j^2] is proportional within a group at first order,
+ *   w_j * e_j compared exactly, ties to the lower token index, slots in ascending token order.
+ * a_h is the mean post-RoPE calibration query of KV head h, pooling its g query heads: f64 sums
+ * in head order, then query order, divided by g * n_cal, rounded to f32.
+ *   q_cal  host f32 [Hq][n_cal][d] (read only)
+ *   a      host f32 [Hkv][d] (written)
+ * Errors: NULL, SHAPE (n_cal < 1), UNSUPPORTED (d), NUMERIC (non-finite input).
+ */
+headq_status headq_calibrate_mean(const headq_config* cfg, const float* q_cal, int64_t n_cal, float* a);
+
+/*
  * headq_cache_append — quantize and store tokens [start, start + n_new) of every (b, h) stream.
  * Summary §3 step 2: base-quantize each key with B_b, take the residual e = k - k_base,
  * project it on U_h and side-quantize the projection with Q_q; the cache keeps the base key and
@@ -152,7 +183,8 @@ headq_status headq_calibrate(const headq_config* cfg, const float* q_cal, int64_
  *   y_i = sum_c U[c][i] e_c as one f32 fma chain over c = 0..d-1 starting from +0
  *   sigma = fp16(max_i |y_i| / 7), zc_i = clamp(rint(y_i * (1/sigma)), -7, 7) (all 0 if sigma == 0)
  * Dense values are copied into the cache layout; 2-bit values get the per-token quantizer over
- * 32-channel groups with the same numerics. Appends may be token-granular: every 32-token group
+ * 32-channel groups with the same numerics, and with value_protect > 0 every encoded group gets
+ * the A^2 value policy's corrections (headq_calibrate_mean; its direction from cache->vdir). Appends may be token-granular: every 32-token group
  * that is whole once tokens [start, start + n_new) are in is encoded (its tokens before `start`
  * are taken from the tails), and the tokens of an unfinished last group are copied exactly into
  * ktail / vtail (rows t % 32). Appends to a stream must be sequential: the tails hold tokens
@@ -300,6 +332,16 @@ static inline size_t headq_page_v_bytes(const headq_config* c) {
 }
 static inline size_t headq_page_vcode_bytes(const headq_config* c) { return (size_t)c->n_kv_heads * c->head_dim * 8; }
 static inline size_t headq_page_vmeta_bytes(const headq_config* c) { return (size_t)c->n_kv_heads * 2 * c->head_dim * 2; }
+static inline size_t headq_vpidx_bytes(const headq_config* c) {
+  return (size_t)c->batch * c->n_kv_heads * (c->capacity / 32) * 4;
+}
+static inline size_t headq_vprot_bytes(const headq_config* c) {
+  return (size_t)c->batch * c->n_kv_heads * (c->capacity / 32) * c->value_protect * c->head_dim * 2;
+}
+static inline size_t headq_page_vpidx_bytes(const headq_config* c) { return (size_t)c->n_kv_heads * 4; }
+static inline size_t headq_page_vprot_bytes(const headq_config* c) {
+  return (size_t)c->n_kv_heads * c->value_protect * c->head_dim * 2;
+}
 static inline size_t headq_ktail_bytes(const headq_config* c) {
   return (size_t)c->batch * c->n_kv_heads * 32 * c->head_dim * (c->key_dtype == HEADQ_F32 ? 4 : 2);
 }

@@ -5,10 +5,10 @@ include/headq.h); this package only marshals arguments to it.
 """
 from .binding import (DIAG_STATS, EXPORTS, HEADQ_BF16, HEADQ_F32, HEADQ_V_DENSE, HEADQ_V_Q2, Config, DeviceCache,
                       HeadQError, PagedDeviceCache, decode_workspace_bytes, diagnostics_workspace_bytes,
-                      headq_cache_append, headq_calibrate, headq_decode_attn, headq_prefill_attn,
+                      headq_cache_append, headq_calibrate, headq_calibrate_mean, headq_decode_attn, headq_prefill_attn,
                       headq_score_diagnostics, load)
 
 __all__ = ["DIAG_STATS", "EXPORTS", "HEADQ_BF16", "HEADQ_F32", "HEADQ_V_DENSE", "HEADQ_V_Q2", "Config", "DeviceCache",
            "HeadQError", "PagedDeviceCache", "decode_workspace_bytes", "diagnostics_workspace_bytes",
-           "headq_cache_append", "headq_calibrate", "headq_decode_attn", "headq_prefill_attn",
+           "headq_cache_append", "headq_calibrate", "headq_calibrate_mean", "headq_decode_attn", "headq_prefill_attn",
            "headq_score_diagnostics", "load"]

@@ -23,8 +23,8 @@ STATUS = {
     0: "HEADQ_OK", 1: "HEADQ_ERR_NULL", 2: "HEADQ_ERR_SHAPE", 3: "HEADQ_ERR_ALIGN", 4: "HEADQ_ERR_CAPACITY",
     5: "HEADQ_ERR_WORKSPACE", 6: "HEADQ_ERR_NUMERIC", 7: "HEADQ_ERR_UNSUPPORTED", 8: "HEADQ_ERR_HIP",
 }
-EXPORTS = ("headq_calibrate", "headq_cache_append", "headq_decode_attn", "headq_prefill_attn",
-           "headq_score_diagnostics", "headq_status_string")
+EXPORTS = ("headq_calibrate", "headq_calibrate_mean", "headq_cache_append", "headq_decode_attn",
+           "headq_prefill_attn", "headq_score_diagnostics", "headq_status_string")
 DIAG_STATS = ("fisher_var", "kl", "mean_ds", "max_abs_ds", "a2", "entropy")  # HEADQ_DIAG_* order
 
 
@@ -40,7 +40,7 @@ class headq_config(ctypes.Structure):
         ("batch", ctypes.c_int32), ("capacity", ctypes.c_int64), ("base_bits", ctypes.c_int32),
         ("group", ctypes.c_int32), ("rank", ctypes.c_int32), ("side_bits", ctypes.c_int32),
         ("key_dtype", ctypes.c_int32), ("value_dtype", ctypes.c_int32), ("value_mode", ctypes.c_int32),
-        ("query_dtype", ctypes.c_int32),
+        ("query_dtype", ctypes.c_int32), ("value_protect", ctypes.c_int32),
     ]
 
 
@@ -50,6 +50,7 @@ class headq_cache(ctypes.Structure):
         ("ssc", ctypes.c_void_p), ("v", ctypes.c_void_p), ("vcode", ctypes.c_void_p),
         ("vmeta", ctypes.c_void_p), ("U", ctypes.c_void_p), ("ktail", ctypes.c_void_p), ("vtail", ctypes.c_void_p),
         ("block_table", ctypes.c_void_p), ("max_pages", ctypes.c_int64), ("n_pages", ctypes.c_int64),
+        ("vdir", ctypes.c_void_p), ("vpidx", ctypes.c_void_p), ("vprot", ctypes.c_void_p),
     ]
 
 
@@ -65,14 +66,15 @@ def load() -> ctypes.CDLL:
         L = ctypes.CDLL(str(LIB_PATH))
         P, I32, I64, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
         L.headq_calibrate.argtypes = [P, P, I64, P, P]
+        L.headq_calibrate_mean.argtypes = [P, P, I64, P]
         L.headq_cache_append.argtypes = [P, P, P, P, P, P, I64, I64, P, P]
         L.headq_decode_attn.argtypes = [P, P, P, I64, P, P, I32, F, P, I32, P, P, P]
         L.headq_score_diagnostics.argtypes = [P, P, P, P, P, P, P, I64, F, P, I32, P, P, P]
         L.headq_prefill_attn.argtypes = [P, P, P, I64, I64, P, I32, F, P, P]
         L.headq_status_string.argtypes = [ctypes.c_int]
         L.headq_status_string.restype = ctypes.c_char_p
-        for fn in ("headq_calibrate", "headq_cache_append", "headq_decode_attn", "headq_prefill_attn",
-                   "headq_score_diagnostics"):
+        for fn in ("headq_calibrate", "headq_calibrate_mean", "headq_cache_append", "headq_decode_attn",
+                   "headq_prefill_attn", "headq_score_diagnostics"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -105,11 +107,12 @@ class Config:
     base_bits: int = 2
     group: int = GROUP
     side_bits: int = 4
+    value_protect: int = 0
 
     def c(self) -> headq_config:
         return headq_config(self.head_dim, self.n_q_heads, self.n_kv_heads, self.batch, self.capacity,
                             self.base_bits, self.group, self.rank, self.side_bits, self.key_dtype,
-                            self.value_dtype, self.value_mode, self.query_dtype)
+                            self.value_dtype, self.value_mode, self.query_dtype, self.value_protect)
 
 
 def _ptr(t) -> int | None:
@@ -139,6 +142,16 @@ def headq_calibrate(cfg: Config, q_cal: np.ndarray):
     _check(load().headq_calibrate(ctypes.byref(c), _ptr(q), q.shape[1], _ptr(U) if cfg.rank else None, _ptr(eig)),
            "headq_calibrate")
     return U, eig
+
+
+def headq_calibrate_mean(cfg: Config, q_cal: np.ndarray):
+    """Host mean calibration query per KV head (the A^2 value policy's direction).
+    q_cal: f32 [Hq][n_cal][d] (numpy). Returns a f32 [Hkv][d]."""
+    q = np.ascontiguousarray(q_cal, dtype=np.float32)
+    a = np.zeros((cfg.n_kv_heads, cfg.head_dim), np.float32)
+    c = cfg.c()
+    _check(load().headq_calibrate_mean(ctypes.byref(c), _ptr(q), q.shape[1], _ptr(a)), "headq_calibrate_mean")
+    return a
 
 
 def _strides3(t):
@@ -241,15 +254,24 @@ class DeviceCache:
         self.ktail = torch.zeros((B, H, GROUP, d), dtype=kdt, device=device)
         self.vtail = torch.zeros((B, H, GROUP, d), dtype=vdt, device=device)
         self.U = None
+        self.vdir = None
+        Pv = cfg.value_protect
+        self.vpidx = torch.zeros((B, H, cap // GROUP), dtype=torch.int32, device=device) if Pv else None
+        self.vprot = torch.zeros((B, H, cap // GROUP, Pv, d), dtype=i16, device=device) if Pv else None
 
     def set_basis(self, U):
         import torch
         self.U = torch.as_tensor(np.ascontiguousarray(U, np.float32)).to(self.kcode.device)
 
+    def set_direction(self, a):
+        """The A^2 value policy's direction (headq_calibrate_mean's output), f32 [Hkv][d]."""
+        import torch
+        self.vdir = torch.as_tensor(np.ascontiguousarray(a, np.float32)).to(self.kcode.device)
+
     def c(self) -> headq_cache:
         return headq_cache(_ptr(self.kcode), _ptr(self.kmeta), _ptr(self.scode), _ptr(self.ssc), _ptr(self.v),
                            _ptr(self.vcode), _ptr(self.vmeta), _ptr(self.U), _ptr(self.ktail), _ptr(self.vtail),
-                           None, 0, 0)
+                           None, 0, 0, _ptr(self.vdir), _ptr(self.vpidx), _ptr(self.vprot))
 
     def append(self, k, v=None, start: int = 0, stream=None, row_start=None):
         headq_cache_append(self.cfg, self.c(), k, v, start, stream, row_start)
@@ -290,7 +312,8 @@ class DeviceCache:
 
     def nbytes(self) -> int:
         return sum(t.numel() * t.element_size() for t in (self.kcode, self.kmeta, self.scode, self.ssc, self.v,
-                                                           self.vcode, self.vmeta, self.ktail, self.vtail)
+                                                           self.vcode, self.vmeta, self.ktail, self.vtail,
+                                                           self.vpidx, self.vprot)
                    if t is not None)
 
 
@@ -325,8 +348,13 @@ class PagedDeviceCache(DeviceCache):
         self.vtail = torch.zeros((cfg.batch, H, GROUP, d), dtype=vdt, device=device)
         self.block_table = torch.zeros((cfg.batch, max_pages), dtype=torch.int32, device=device)
         self.U = None
+        self.vdir = None
+        Pv = cfg.value_protect
+        self.vpidx = torch.zeros((P, H), dtype=torch.int32, device=device) if Pv else None
+        self.vprot = torch.zeros((P, H, Pv, d), dtype=i16, device=device) if Pv else None
 
     def c(self) -> headq_cache:
         return headq_cache(_ptr(self.kcode), _ptr(self.kmeta), _ptr(self.scode), _ptr(self.ssc), _ptr(self.v),
                            _ptr(self.vcode), _ptr(self.vmeta), _ptr(self.U), _ptr(self.ktail), _ptr(self.vtail),
-                           _ptr(self.block_table), self.max_pages, self.n_pages)
+                           _ptr(self.block_table), self.max_pages, self.n_pages, _ptr(self.vdir), _ptr(self.vpidx),
+                           _ptr(self.vprot))

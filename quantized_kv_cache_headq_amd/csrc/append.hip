@@ -20,6 +20,12 @@
 //   5. values (when given): dense values are transposed into the channel-major group layout
 //      (8 tokens of a channel per 16-byte store), 2-bit values quantized per (token, 32-channel
 //      group) into the matrix-operand layout.
+//   6. A^2 value policy (2-bit values, value_protect = P > 0; reading of the summary's §2.2 A^2
+//      surrogate and §5 A^2-weighted value policy): per group, the P tokens of largest w_j * e_j
+//      keep a bfloat16 correction v_j - v_hat_j. e_j = |v_j - v_hat_j|^2 (one f32 fma chain over
+//      the channels), w_j = 2^n_j with n_j = clamp(rint(c2 * a_h.k_j), -64, 64) taken from the
+//      keys in step 2 (a_h the mean calibration query, a_h.k_j one f32 fma chain); the products are
+//      compared exactly in f64, ties to the lower token, slots in ascending token order.
 //
 // Numerics: no contraction anywhere in this file (every fma is explicit), IEEE division,
 // rint = round half to even, binary16 conversion with round to nearest even.
@@ -171,6 +177,10 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
   __shared__ float s_s[GPW * D], z_s[GPW * D], inv_s[GPW * D];
   __shared__ float amax_s[SLOTS][kRows];
   __shared__ float U_s[UL && R > 0 ? D * R : 1];
+  __shared__ int pn_s[kRows];              // A^2 value policy: weight exponent per token row
+  __shared__ double pr_s[kRows];           //   w_j * e_j
+  __shared__ int sel_s[kRows];             //   chosen
+  __shared__ int tok_s[GPW][2];            //   token of each slot
 
   const int h = blockIdx.y, b = blockIdx.z;
   const float klev = (float)a.key_levels;  // base-code levels of the keys (values are 2-bit: 3)
@@ -234,6 +244,19 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
     s_s[i] = s;
     z_s[i] = z;
     inv_s[i] = inv;
+  }
+  // the A^2 value policy's weight exponent of each row, from the keys (step 3 replaces them by
+  // residuals); the last kRows threads, the ones step 2 leaves idle for one-group launches
+  const bool prot = a.value_protect > 0 && a.v != nullptr;
+  if (prot && tid >= kThreads - kRows) {
+    const int row = tid - (kThreads - kRows);
+    const const_f32_ptr ad = (const_f32_ptr)(a.vdir + (int64_t)h * D);
+    float dot = 0.0f;
+    for (int c = 0; c < D; ++c) dot = __builtin_fmaf(ad[c], ke[row][c], dot);
+    float nf = __builtin_rintf(dot * a.prot_c2);
+    nf = nf < -64.0f ? -64.0f : nf;
+    nf = nf > 64.0f ? 64.0f : nf;
+    pn_s[row] = (int)nf;
   }
   __syncthreads();
 
@@ -429,6 +452,54 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
           v |= base_code(ke[row][c], z_s[row * NG + gc], inv_s[row * NG + gc], 3.0f) << (4 * e + 2 * q);
         }
       if (tl.whole(gl)) a.vcode[a.map.block(b, h, tl.group(gl)) * D * 8 + byte] = (uint8_t)v;
+    }
+    if (prot) {
+      // 6. the A^2 value policy: w_j * e_j per row (reads what the code loop reads)
+      if (tid < kRows) {
+        const int row = tid;
+        float e = 0.0f;
+        for (int c = 0; c < D; ++c) {
+          const int m = row * NG + c / 32;
+          const uint32_t code = base_code(ke[row][c], z_s[m], inv_s[m], 3.0f);
+          const float diff = ke[row][c] - __builtin_fmaf((float)code, s_s[m], z_s[m]);
+          e = __builtin_fmaf(diff, diff, e);
+        }
+        pr_s[row] = ldexp((double)e, pn_s[row]);
+      }
+      __syncthreads();
+      const int NP = a.value_protect;
+      if (tid < kRows) {
+        const int gl = tid / kGroup, t = tid % kGroup;
+        const double me = pr_s[tid];
+        int rank = 0;
+        for (int u = 0; u < kGroup; ++u) {
+          const double o = pr_s[gl * kGroup + u];
+          rank += (o > me || (o == me && u < t)) ? 1 : 0;
+        }
+        sel_s[tid] = rank < NP;
+      }
+      __syncthreads();
+      if (tid < kRows && sel_s[tid]) {
+        const int gl = tid / kGroup, t = tid % kGroup;
+        int slot = 0;
+        for (int u = 0; u < t; ++u) slot += sel_s[gl * kGroup + u];
+        tok_s[gl][slot] = t;
+      }
+      __syncthreads();
+      if (tid < GPW && tl.whole(tid)) {
+        uint32_t word = 0;
+        for (int k = 0; k < NP; ++k) word |= (uint32_t)tok_s[tid][k] << (8 * k);
+        a.vpidx[a.map.block(b, h, tl.group(tid))] = word;
+      }
+      for (int i = tid; i < GPW * NP * D; i += kThreads) {
+        const int gl = i / (NP * D), k = (i / D) % NP, c = i % D;
+        if (!tl.whole(gl)) continue;
+        const int row = gl * kGroup + tok_s[gl][k];
+        const int m = row * NG + c / 32;
+        const uint32_t code = base_code(ke[row][c], z_s[m], inv_s[m], 3.0f);
+        const float dlt = ke[row][c] - __builtin_fmaf((float)code, s_s[m], z_s[m]);
+        a.vprot[(a.map.block(b, h, tl.group(gl)) * NP + k) * D + c] = __builtin_bit_cast(uint16_t, (__bf16)dlt);
+      }
     }
   }
   }  // values

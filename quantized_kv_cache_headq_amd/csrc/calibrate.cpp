@@ -183,3 +183,21 @@ extern "C" headq_status headq_calibrate(const headq_config* cfg, const float* q_
   }
   return HEADQ_OK;
 }
+
+extern "C" headq_status headq_calibrate_mean(const headq_config* cfg, const float* q_cal, int64_t n_cal, float* a) {
+  if (!cfg || !q_cal || !a) return HEADQ_ERR_NULL;
+  const int d = cfg->head_dim, hq = cfg->n_q_heads, hkv = cfg->n_kv_heads;
+  if (d != 64 && d != 128) return HEADQ_ERR_UNSUPPORTED;
+  if (hq < 1 || hkv < 1 || hq % hkv || n_cal < 1) return HEADQ_ERR_SHAPE;
+  for (int64_t i = 0; i < (int64_t)hq * n_cal * d; ++i)
+    if (!std::isfinite(q_cal[i])) return HEADQ_ERR_NUMERIC;
+  const int g = hq / hkv;
+  for (int h = 0; h < hkv; ++h)
+    for (int c = 0; c < d; ++c) {
+      double acc = 0.0;
+      for (int hh = h * g; hh < (h + 1) * g; ++hh)
+        for (int64_t n = 0; n < n_cal; ++n) acc += (double)q_cal[((int64_t)hh * n_cal + n) * d + c];
+      a[(int64_t)h * d + c] = (float)(acc / ((double)g * (double)n_cal));
+    }
+  return HEADQ_OK;
+}

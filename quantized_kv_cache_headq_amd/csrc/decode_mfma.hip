@@ -82,6 +82,7 @@ __device__ __forceinline__ void lds_wave_fence() {
 // Wave-uniform view of one (b, h) stream of the cache.
 struct Stream {
   __amdgpu_buffer_rsrc_t kcode, kmeta, scode, ssc, v, vmeta;
+  __amdgpu_buffer_rsrc_t vprot, vpidx;  // A^2 value policy (VP > 0)
 };
 
 // Bytes of one 32-token group staged per wave in LDS, in this order:
@@ -198,6 +199,58 @@ __device__ __forceinline__ void load_group(GroupRaw<D, R, VQ2, NB>& g, const Str
 __device__ __forceinline__ int request_page(const DecodeArgs& a, __amdgpu_buffer_rsrc_t table_row, int gi) {
   const int off = __builtin_amdgcn_readfirstlane(gi * 4);  // wave-uniform: no loop over the lanes
   return a.map.block_table ? (int)__builtin_amdgcn_raw_buffer_load_b32(table_row, 0, off, 0) : 0;
+}
+
+// A^2 value policy, VP corrected tokens per group (2-bit values): the lane's share of the group's
+// [VP][d] bfloat16 corrections (staged in LDS like the key side) and the group's token indices.
+template <int D, int VP>
+struct ProtRaw {
+  typename Bytes<(VP > 0 ? VP * D / 32 : 4)>::T vp;
+  uint32_t idx;  // slot k: bits 8k .. 8k+7
+};
+
+template <int D, int R, bool NB, int VP>
+__device__ __forceinline__ void load_prot(ProtRaw<D, VP>& p, const Stream& s_stream, const DecodeArgs& a, int h,
+                                          int page_v, int lane, int gi_in) {
+  constexpr int BYTES = VP * D * 2;
+  int gi = __builtin_amdgcn_readfirstlane(gi_in);
+  __amdgpu_buffer_rsrc_t rp = s_stream.vprot, ri = s_stream.vpidx;
+  if (a.map.block_table) {
+    int64_t page = __builtin_amdgcn_readfirstlane(page_v);
+    page = page < 0 ? 0 : (page >= a.map.n_pages ? a.map.n_pages - 1 : page);
+    const int64_t blk = page * a.hkv + h;
+    rp = make_rsrc(a.vprot + blk * VP * D, BYTES);
+    ri = make_rsrc(a.vpidx + blk, 4);
+    gi = 0;
+  }
+  p.vp = load_piece<VP * D / 32>(rp, lane * (VP * D / 32), gi * BYTES);
+  p.idx = __builtin_amdgcn_raw_buffer_load_b32(ri, 0, gi * 4, kStream);
+}
+
+// o += p_t * correction_t for the corrected tokens t of the lane's group (rows staged at `prow`,
+// [VP][d] bf16). Token t's probability for this column is held by the lane of the same column
+// with quad t / 8, slot t % 8; every lane of a column shares the group, hence the token list.
+template <int D, int VP>
+__device__ __forceinline__ void add_corrections(const uint8_t* prow, uint32_t idx, const float* p, int n, int quad,
+                                                floatx4* o_acc) {
+  constexpr int NCT = D / 16;
+#pragma unroll
+  for (int k = 0; k < VP; ++k) {
+    const int t = (idx >> (8 * k)) & 31;
+    float pt = p[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) pt = (t & 7) == j ? p[j] : pt;
+    pt = __shfl(pt, n + 16 * (t >> 3));
+    const uint16_t* row = reinterpret_cast<const uint16_t*>(prow + k * D * 2);
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const u32x2 w = *reinterpret_cast<const u32x2*>(row + 16 * ct + 4 * quad);  // channels 16ct + 4quad ..+3
+      o_acc[ct][0] = fmaf(pt, __uint_as_float(w[0] << 16), o_acc[ct][0]);
+      o_acc[ct][1] = fmaf(pt, __uint_as_float(w[0] & 0xffff0000u), o_acc[ct][1]);
+      o_acc[ct][2] = fmaf(pt, __uint_as_float(w[1] << 16), o_acc[ct][2]);
+      o_acc[ct][3] = fmaf(pt, __uint_as_float(w[1] & 0xffff0000u), o_acc[ct][3]);
+    }
+  }
 }
 
 // Per-lane operands fixed for the whole kernel.
@@ -408,14 +461,17 @@ __device__ __forceinline__ void value_operands(const uint8_t* slot, const float*
   }
 }
 
-// One 32-token group: scores, online-softmax update, P.V accumulation.
-template <int D, int R, bool VQ2, bool NB>
-__device__ __forceinline__ void process_group(const GroupRaw<D, R, VQ2, NB>& cur, const Fixed<D, R>& f, uint8_t* slot,
+// One 32-token group: scores, online-softmax update, P.V accumulation (VP > 0: plus the A^2 value
+// policy's corrections, staged at `pslot`).
+template <int D, int R, bool VQ2, bool NB, int VP>
+__device__ __forceinline__ void process_group(const GroupRaw<D, R, VQ2, NB>& cur, const ProtRaw<D, VP>& pr,
+                                              const Fixed<D, R>& f, uint8_t* slot, uint8_t* pslot,
                                               const DecodeArgs& a, int gi, int b, int hq0, int g, int lane, int n,
                                               int quad, floatx4* o_acc, float* z_acc, float& m_run, float& l_run) {
   constexpr int NKT = D / 32, NCT = D / 16, NG = D / 32;
   lds_wave_fence();
   stage_group<D, R, VQ2, NB>(cur, slot, lane);
+  if constexpr (VP > 0) *reinterpret_cast<typename Bytes<VP * D / 32>::T*>(pslot + lane * (VP * D / 32)) = pr.vp;
   lds_wave_fence();
   floatx4 acc[2], cr[2];
   group_logits<D, R, VQ2, NB, false>(slot, f, nullptr, nullptr, n, quad, acc, cr);
@@ -443,6 +499,7 @@ __device__ __forceinline__ void process_group(const GroupRaw<D, R, VQ2, NB>& cur
       o_acc[2 * cg + 1] = mfma_bf16(a1, bh[cg], o_acc[2 * cg + 1]);
       o_acc[2 * cg + 1] = mfma_bf16(a1, bl[cg], o_acc[2 * cg + 1]);
     }
+    if constexpr (VP > 0) add_corrections<D, VP>(pslot, pr.idx, p, n, quad, o_acc);
   } else {
     bf16x8_t p_hi8, p_lo8;
 #pragma unroll
@@ -470,11 +527,12 @@ __device__ __forceinline__ void process_group(const GroupRaw<D, R, VQ2, NB>& cur
 // products of all J groups run unconditionally (straight-line code the scheduler can interleave),
 // a missing group's results are only ever selected by idle columns, whose scores are replaced and
 // whose probabilities are 0, and its value operand meets zero columns only.
-template <int D, int R, bool NB, int J>
-__device__ __forceinline__ void process_block(const typename Bytes<D / 8>::T* vcs, const int* gis, int nv,
-                                              const Fixed<D, R>& f, const uint8_t* slots, const DecodeArgs& a, int b,
-                                              int hq0, int g, int jl, int hd, int n, int quad, floatx4* o_acc,
-                                              float* z_acc, float& m_run, float& l_run) {
+template <int D, int R, bool NB, int J, int VP>
+__device__ __forceinline__ void process_block(const typename Bytes<D / 8>::T* vcs, const uint32_t* pidx,
+                                              const int* gis, int nv, const Fixed<D, R>& f, const uint8_t* slots,
+                                              const uint8_t* pslots, const DecodeArgs& a, int b, int hq0, int g,
+                                              int jl, int hd, int n, int quad, floatx4* o_acc, float* z_acc,
+                                              float& m_run, float& l_run) {
   constexpr int NKT = D / 32, NCT = D / 16, NG = D / 32;
   using KS = KSide<D, R, true, NB>;
   const bool live = jl < nv;
@@ -523,6 +581,14 @@ __device__ __forceinline__ void process_block(const typename Bytes<D / 8>::T* vc
       o_acc[2 * cg + 1] = mfma_bf16(a1, bhj, o_acc[2 * cg + 1]);
       o_acc[2 * cg + 1] = mfma_bf16(a1, blj, o_acc[2 * cg + 1]);
     }
+  }
+  if constexpr (VP > 0) {
+    // the corrections of the lane's own group (idle columns: p = 0 against finite rows)
+    const int jo = live ? jl : nv - 1;
+    uint32_t idx = pidx[0];
+#pragma unroll
+    for (int j = 1; j < J; ++j) idx = jo == j ? pidx[j] : idx;
+    add_corrections<D, VP>(pslots + jo * (VP * D * 2), idx, p, n, quad, o_acc);
   }
 }
 
@@ -633,16 +699,20 @@ __device__ __forceinline__ void process_tail(const DecodeArgs& a, int64_t n_ctx,
 }
 
 // J > 1: J groups per step share the matrix columns (2-bit values, g <= 16 / J; see process_block).
-template <int D, int R, bool VQ2, bool NB, int J>
+// VP > 0: the A^2 value policy's VP corrected tokens per group (2-bit values and 2-bit keys).
+template <int D, int R, bool VQ2, bool NB, int J, int VP>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_mfma_kernel(DecodeArgs a) {
   static_assert(J == 1 || VQ2, "packed columns are built for 2-bit values");
+  static_assert(VP == 0 || (VQ2 && !NB), "the value policy is built for 2-bit values and 2-bit keys");
   constexpr int NKT = D / 32, NCT = D / 16, NG = D / 32;
   constexpr int RU = R > 0 ? R : 1;
   constexpr int SLOT = KSide<D, R, VQ2, NB>::BYTES;
+  constexpr int PSLOT = VP * D * 2;            // corrections of one group
   __shared__ float qs[kMaxGqa][D];            // scaled queries
   __shared__ float qu_s[kMaxGqa][RU];         // U^T q (scaled)
   __shared__ float inv_scale_s[kMaxGqa];      // 2^e undoing the per-head query scale
   __shared__ u32x4 kslot[kWaves][J * SLOT / 16];  // per-wave staging of the groups of a step
+  __shared__ u32x4 pslot_s[kWaves][VP > 0 ? J * PSLOT / 16 : 1];  // their corrections
   __shared__ float m_w[kWaves][kMaxGqa], l_w[kWaves][kMaxGqa];
   __shared__ float o_w[kWaves][kMaxGqa][D];
 
@@ -695,6 +765,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     s.v = make_rsrc((const uint16_t*)a.vdense + bh * a.cap * D, a.cap * D * 2);
     s.vmeta = s.v;
   }
+  if constexpr (VP > 0) {
+    s.vprot = make_rsrc(a.vprot + bh * groups_cap * VP * D, (int64_t)groups_cap * PSLOT);
+    s.vpidx = make_rsrc(a.vpidx + bh * groups_cap, (int64_t)groups_cap * 4);
+  }
   // group indices are 32-bit and wave-uniform, so every offset below stays in scalar registers
   // this row's attended tokens: whole groups, then the unfinished one from the tails
   int64_t n_ctx = a.n_ctx;
@@ -725,19 +799,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   GroupRaw<D, R, VQ2, NB> ga, gb;  // ping-pong register sets: one group computed while the next loads
   GroupRaw<D, R, VQ2, NB> gj[J];   // J > 1: the next step's groups, loaded while a step computes
   int pj[J];                       // J > 1: their pages (paged caches), requested one step ahead
+  ProtRaw<D, VP> qa, qb, qj[J];    // VP > 0: the policy's corrections of ga, gb, gj
+  // one group's loads (and its corrections) into register set g / q
+  auto load = [&](GroupRaw<D, R, VQ2, NB>& gr, ProtRaw<D, VP>& qr, int page, int gi) {
+    load_group<D, R, VQ2, NB>(gr, s, a, h, page, lane, n, quad, gi);
+    if constexpr (VP > 0) load_prot<D, R, NB, VP>(qr, s, a, h, page, lane, gi);
+  };
   auto first_loads = [&]() {
     if constexpr (J == 1) {
-      if (j_begin < n_groups)
-        load_group<D, R, VQ2, NB>(ga, s, a, h, page_at(j_begin), lane, n, quad, group_at(j_begin));
-      if (j_begin + W < n_groups)
-        load_group<D, R, VQ2, NB>(gb, s, a, h, page_at(j_begin + W), lane, n, quad, group_at(j_begin + W));
+      if (j_begin < n_groups) load(ga, qa, page_at(j_begin), group_at(j_begin));
+      if (j_begin + W < n_groups) load(gb, qb, page_at(j_begin + W), group_at(j_begin + W));
       pa = page_at(j_begin + 2 * W);
       pb = page_at(j_begin + 3 * W);
     } else {
 #pragma unroll
       for (int j = 0; j < J; ++j) {
         const int sl = j_begin + W * j;
-        if (sl < n_groups) load_group<D, R, VQ2, NB>(gj[j], s, a, h, page_at(sl), lane, n, quad, group_at(sl));
+        if (sl < n_groups) load(gj[j], qj[j], page_at(sl), group_at(sl));
       }
 #pragma unroll
       for (int j = 0; j < J; ++j) pj[j] = page_at(j_begin + W * (J + j));
@@ -818,6 +896,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
   // ---- this wave's groups
   uint8_t* slot = reinterpret_cast<uint8_t*>(kslot[wave]);
+  uint8_t* pslot = reinterpret_cast<uint8_t*>(pslot_s[wave]);
   if constexpr (J > 1) {
     // steps of J groups (the wave's group slots j_begin + W*k, k = k0 .. k0+J-1): stage the
     // step's groups, request the next step's, compute this one from LDS
@@ -832,32 +911,43 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       lds_wave_fence();
 #pragma unroll
       for (int j = 0; j < J; ++j)
-        if (j < nv) stage_group<D, R, VQ2, NB>(gj[j], slot + j * SLOT, lane);
+        if (j < nv) {
+          stage_group<D, R, VQ2, NB>(gj[j], slot + j * SLOT, lane);
+          if constexpr (VP > 0)
+            *reinterpret_cast<typename Bytes<VP * D / 32>::T*>(pslot + j * PSLOT + lane * (VP * D / 32)) = qj[j].vp;
+        }
       lds_wave_fence();
       typename Bytes<D / 8>::T vcs[J];
+      uint32_t pidx[J];
 #pragma unroll
-      for (int j = 0; j < J; ++j) vcs[j] = gj[j].vc;
+      for (int j = 0; j < J; ++j) {
+        vcs[j] = gj[j].vc;
+        pidx[j] = qj[j].idx;
+      }
 #pragma unroll
       for (int j = 0; j < J; ++j) {
         const int sl = j_begin + W * (k0 + J + j);
-        if (sl < n_groups) load_group<D, R, VQ2, NB>(gj[j], s, a, h, pj[j], lane, n, quad, group_at(sl));
+        if (sl < n_groups) load(gj[j], qj[j], pj[j], group_at(sl));
       }
 #pragma unroll
       for (int j = 0; j < J; ++j) pj[j] = page_req(j_begin + W * (k0 + 2 * J + j));
-      process_block<D, R, NB, J>(vcs, gis, nv, f, slot, a, b, hq0, g, jl, hd, n, quad, o_acc, z_acc, m_run, l_run);
+      process_block<D, R, NB, J, VP>(vcs, pidx, gis, nv, f, slot, pslot, a, b, hq0, g, jl, hd, n, quad, o_acc, z_acc,
+                                     m_run, l_run);
     }
   } else
   for (int j = j_begin; j < n_groups; j += 2 * W) {
-    process_group<D, R, VQ2, NB>(ga, f, slot, a, group_at(j), b, hq0, g, lane, n, quad, o_acc, z_acc, m_run, l_run);
+    process_group<D, R, VQ2, NB, VP>(ga, qa, f, slot, pslot, a, group_at(j), b, hq0, g, lane, n, quad, o_acc, z_acc,
+                                     m_run, l_run);
     if (j + W >= n_groups) break;
     if (j + 2 * W < n_groups) {
-      load_group<D, R, VQ2, NB>(ga, s, a, h, pa, lane, n, quad, group_at(j + 2 * W));
+      load(ga, qa, pa, group_at(j + 2 * W));
       pa = page_at(j + 4 * W);
     }
-    process_group<D, R, VQ2, NB>(gb, f, slot, a, group_at(j + W), b, hq0, g, lane, n, quad, o_acc, z_acc, m_run,
+    process_group<D, R, VQ2, NB, VP>(gb, qb, f, slot, pslot, a, group_at(j + W), b, hq0, g, lane, n, quad, o_acc, z_acc,
+                                     m_run,
                              l_run);
     if (j + 3 * W < n_groups) {
-      load_group<D, R, VQ2, NB>(gb, s, a, h, pb, lane, n, quad, group_at(j + 3 * W));
+      load(gb, qb, pb, group_at(j + 3 * W));
       pb = page_at(j + 5 * W);
     }
   }
@@ -972,27 +1062,40 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   if (tid == 0) atomicExch(a.ws_count + bh, 0u);
 }
 
-template <int D, bool VQ2, bool NB, int J>
-hipError_t launch_rj(const DecodeArgs& a, hipStream_t s) {
+template <int D, bool VQ2, bool NB, int J, int VP>
+hipError_t launch_rjp(const DecodeArgs& a, hipStream_t s) {
   dim3 grid((unsigned)a.n_splits, (unsigned)a.hkv, (unsigned)a.batch);
   switch (a.r) {
-    case 0: hipLaunchKernelGGL((decode_mfma_kernel<D, 0, VQ2, NB, J>), grid, dim3(kThreads), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((decode_mfma_kernel<D, 4, VQ2, NB, J>), grid, dim3(kThreads), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((decode_mfma_kernel<D, 8, VQ2, NB, J>), grid, dim3(kThreads), 0, s, a); break;
-    case 16: hipLaunchKernelGGL((decode_mfma_kernel<D, 16, VQ2, NB, J>), grid, dim3(kThreads), 0, s, a); break;
-    case 32: hipLaunchKernelGGL((decode_mfma_kernel<D, 32, VQ2, NB, J>), grid, dim3(kThreads), 0, s, a); break;
+    case 0: hipLaunchKernelGGL((decode_mfma_kernel<D, 0, VQ2, NB, J, VP>), grid, dim3(kThreads), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((decode_mfma_kernel<D, 4, VQ2, NB, J, VP>), grid, dim3(kThreads), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((decode_mfma_kernel<D, 8, VQ2, NB, J, VP>), grid, dim3(kThreads), 0, s, a); break;
+    case 16: hipLaunchKernelGGL((decode_mfma_kernel<D, 16, VQ2, NB, J, VP>), grid, dim3(kThreads), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((decode_mfma_kernel<D, 32, VQ2, NB, J, VP>), grid, dim3(kThreads), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-// 2-bit values with few heads per KV head: J = 16 / g groups (at most 3) share the matrix columns.
+template <int D, bool VQ2, bool NB, int J>
+hipError_t launch_rj(const DecodeArgs& a, hipStream_t s) {
+  if constexpr (VQ2 && !NB && J <= 2) {
+    if (a.value_protect == 1) return launch_rjp<D, true, false, J, 1>(a, s);
+    if (a.value_protect == 2) return launch_rjp<D, true, false, J, 2>(a, s);
+  }
+  if (a.value_protect) return hipErrorInvalidValue;
+  return launch_rjp<D, VQ2, NB, J, 0>(a, s);
+}
+
+// 2-bit values with few heads per KV head: J = 16 / g groups share the matrix columns, at most 3
+// for d = 128 with 2-bit keys and no value policy, at most 2 otherwise (three groups in flight
+// would spill registers there).
 template <int D, bool VQ2, bool NB>
 hipError_t launch_r(const DecodeArgs& a, hipStream_t s) {
   if constexpr (VQ2) {
     const int j = a.pack_columns ? (a.gqa <= 5 ? 3 : a.gqa <= 8 ? 2 : 1) : 1;
-    if (j == 3) return launch_rj<D, true, NB, 3>(a, s);
-    if (j == 2) return launch_rj<D, true, NB, 2>(a, s);
+    if constexpr (D == 128 && !NB)
+      if (j == 3 && a.value_protect == 0) return launch_rj<D, true, NB, 3>(a, s);
+    if (j >= 2) return launch_rj<D, true, NB, 2>(a, s);
   }
   return launch_rj<D, VQ2, NB, 1>(a, s);
 }

@@ -2,6 +2,7 @@
 //
 // Every check runs on the host before the first HIP call, so a rejected call enqueues nothing.
 // The library allocates no device memory: the caller passes the cache and the workspace.
+#include <cmath>
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
@@ -46,6 +47,8 @@ headq_status check_config(const headq_config* c) {
       (c->query_dtype != HEADQ_F32 && c->query_dtype != HEADQ_BF16))
     return HEADQ_ERR_UNSUPPORTED;
   if (c->value_mode != HEADQ_V_DENSE && c->value_mode != HEADQ_V_Q2) return HEADQ_ERR_UNSUPPORTED;
+  if (c->value_protect < 0 || c->value_protect > 2) return HEADQ_ERR_UNSUPPORTED;
+  if (c->value_protect && (c->value_mode != HEADQ_V_Q2 || c->base_bits != 2)) return HEADQ_ERR_UNSUPPORTED;
   return HEADQ_OK;
 }
 
@@ -56,8 +59,9 @@ headq_status check_cache(const headq_config* c, const headq_cache* k) {
   if (c->rank > 0 && (!k->scode || !k->ssc || !k->U)) return HEADQ_ERR_NULL;
   if (c->value_mode == HEADQ_V_DENSE && !k->v) return HEADQ_ERR_NULL;
   if (c->value_mode == HEADQ_V_Q2 && (!k->vcode || !k->vmeta)) return HEADQ_ERR_NULL;
-  const void* ptrs[] = {k->kcode, k->kmeta, k->scode, k->ssc, k->v, k->vcode, k->vmeta, k->U, k->ktail, k->vtail,
-                        k->block_table};
+  if (c->value_protect && (!k->vdir || !k->vpidx || !k->vprot)) return HEADQ_ERR_NULL;
+  const void* ptrs[] = {k->kcode, k->kmeta, k->scode, k->ssc, k->v,     k->vcode, k->vmeta,
+                        k->U,     k->ktail, k->vtail, k->block_table, k->vdir, k->vpidx, k->vprot};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return HEADQ_ERR_ALIGN;
   return HEADQ_OK;
@@ -157,6 +161,11 @@ extern "C" headq_status headq_cache_append(const headq_config* cfg, const headq_
   a.vtail = cache->vtail;
   a.row_start = row_start;
   a.map = map_of(cfg, cache);
+  a.value_protect = cfg->value_protect;
+  a.prot_c2 = (float)(2.0 * 1.4426950408889634 / std::sqrt((double)cfg->head_dim));
+  a.vdir = cache->vdir;
+  a.vpidx = cache->vpidx;
+  a.vprot = cache->vprot;
   hipStream_t s = (hipStream_t)stream;
   return finish(headq::launch_append(a, s), s);
 }
@@ -217,6 +226,7 @@ extern "C" headq_status headq_decode_attn(const headq_config* cfg, const headq_c
   const int64_t n_units = n_groups + (n_ctx % headq::kGroup ? 1 : 0);
   if (n_splits < 0 || n_splits > n_units) return HEADQ_ERR_SHAPE;
   const bool mfma = decode_uses_mfma(cfg);
+  if (cfg->value_protect && !mfma) return HEADQ_ERR_UNSUPPORTED;  // the policy is read by the matrix-core kernel
   const int chunks = mfma ? 4 : 1;
   const int S = n_splits ? n_splits : auto_splits(cfg, n_units, chunks, mfma);
   if (mfma && S > headq::kMaxSplitsMfma) return HEADQ_ERR_UNSUPPORTED;
@@ -264,6 +274,9 @@ extern "C" headq_status headq_decode_attn(const headq_config* cfg, const headq_c
   a.U = cache->U;
   a.ktail = cache->ktail;
   a.vtail = cache->vtail;
+  a.value_protect = cfg->value_protect;
+  a.vpidx = cache->vpidx;
+  a.vprot = cache->vprot;
   a.key_bf16 = cfg->key_dtype == HEADQ_BF16;
   a.row_len = row_len;
   a.map = map_of(cfg, cache);
@@ -284,6 +297,7 @@ extern "C" headq_status headq_score_diagnostics(const headq_config* cfg, const h
   headq_status st = check_config(cfg);
   if (st != HEADQ_OK) return st;
   if (!ws_bytes) return HEADQ_ERR_NULL;
+  if (cfg->value_protect) return HEADQ_ERR_UNSUPPORTED;  // the A^2 value policy is read by the decode only
   if (n_ctx < 1) return HEADQ_ERR_SHAPE;
   if (n_ctx > cfg->capacity) return HEADQ_ERR_CAPACITY;
   const int64_t n_chunks = (n_ctx + 63) / 64;  // 64-token chunks, one wave each at a time
@@ -379,6 +393,7 @@ extern "C" headq_status headq_prefill_attn(const headq_config* cfg, const headq_
   if (out_dtype != HEADQ_F32 && out_dtype != HEADQ_BF16) return HEADQ_ERR_UNSUPPORTED;
   // the matrix-core formats: dense bf16 or 2-bit values
   if (cfg->value_mode == HEADQ_V_DENSE && cfg->value_dtype != HEADQ_BF16) return HEADQ_ERR_UNSUPPORTED;
+  if (cfg->value_protect) return HEADQ_ERR_UNSUPPORTED;  // the A^2 value policy is read by the decode only
   if ((start + n_q) % headq::kGroup && (!cache->ktail || !cache->vtail)) return HEADQ_ERR_NULL;
   if (!aligned16(q) || !aligned16(out) || (logits_dbg && !aligned16(logits_dbg))) return HEADQ_ERR_ALIGN;
 

@@ -79,6 +79,11 @@ struct AppendArgs {
   void* vtail;                 // [B][Hkv][32][d] value_dtype
   const int32_t* row_start;    // [B] per-row append position, or null (all rows at `start`)
   CacheMap map;
+  int value_protect;           // A^2 value policy: corrected tokens per group (0 = off)
+  float prot_c2;               // its weight scale, f32(2 log2(e) / sqrt(d))
+  const float* vdir;           // [Hkv][d] its direction
+  uint32_t* vpidx;             // per group block: the corrected tokens' indices, one per byte
+  uint16_t* vprot;             // per group block: [P][d] bf16 corrections
 };
 
 struct DecodeArgs {
@@ -103,6 +108,9 @@ struct DecodeArgs {
   const float* U;
   const void* ktail;           // tail of the unfinished group (n_ctx % 32 tokens), exact
   const void* vtail;
+  const uint32_t* vpidx;       // A^2 value policy (value_protect > 0): indices per group block
+  const uint16_t* vprot;       //   and [P][d] bf16 corrections per group block
+  int value_protect;
   int key_bf16;                // dtype of ktail
   const int32_t* row_len;      // [B] per-row attended tokens (<= n_ctx), or null (all n_ctx)
   CacheMap map;

@@ -20,12 +20,13 @@ def say(*a):
     sys.stdout.flush()
 
 
-def config(w: synth.Workload, batch=None, cap=None):
+def config(w: synth.Workload, batch=None, cap=None, value_protect=0):
     import quantized_kv_cache_headq_amd as hq
     return hq.Config(head_dim=w.head_dim, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads,
                      batch=w.batch if batch is None else batch, capacity=w.n_ctx if cap is None else cap,
                      rank=w.rank, key_dtype=DT[w.key_dtype], value_dtype=DT[w.value_dtype],
-                     value_mode=VMODE[w.value_mode], query_dtype=DT[w.query_dtype], base_bits=w.base_bits)
+                     value_mode=VMODE[w.value_mode], query_dtype=DT[w.query_dtype], base_bits=w.base_bits,
+                     value_protect=value_protect)
 
 
 def torch_dtype(name):
@@ -39,8 +40,10 @@ def to_device(x_f32: np.ndarray, dtype_name: str):
     return torch.from_numpy(np.ascontiguousarray(x_f32, np.float32)).to("cuda").to(torch_dtype(dtype_name))
 
 
-def gpu_cache(w: synth.Workload, U, batch=None, T=None, cap=None, K=None, V=None, pieces=None):
-    """Allocate a DeviceCache, set U, and append the workload's keys/values (optionally in pieces
+def gpu_cache(w: synth.Workload, U, batch=None, T=None, cap=None, K=None, V=None, pieces=None, value_protect=0,
+              a_dir=None):
+    """Allocate a DeviceCache, set U (and the A^2 value policy's direction a_dir when
+    value_protect > 0), and append the workload's keys/values (optionally in pieces
     [(start, n), ...]). Returns (DeviceCache, K f32 numpy, V f32 numpy)."""
     import quantized_kv_cache_headq_amd as hq
     B = w.batch if batch is None else batch
@@ -50,9 +53,11 @@ def gpu_cache(w: synth.Workload, U, batch=None, T=None, cap=None, K=None, V=None
         K = synth.stack_streams(w, "keys", B, T)
     if V is None:
         V = synth.stack_streams(w, "values", B, T)
-    dc = hq.DeviceCache(config(w, B, cap))
+    dc = hq.DeviceCache(config(w, B, cap, value_protect))
     if w.rank:
         dc.set_basis(U)
+    if value_protect:
+        dc.set_direction(a_dir)
     Kd = to_device(K, w.key_dtype)
     Vd = to_device(V, w.value_dtype)
     for start, n in (pieces or [(0, T)]):
@@ -72,12 +77,15 @@ def host(t, view_u16=False):
 def compare_cache(dc, oc, streams=None):
     """Bit-exact comparison of every cache buffer (optionally only some (b, h) streams)."""
     pairs = [("kcode", dc.kcode), ("kmeta", dc.kmeta), ("scode", dc.scode), ("ssc", dc.ssc), ("v", dc.v),
-             ("vcode", dc.vcode), ("vmeta", dc.vmeta), ("ktail", dc.ktail), ("vtail", dc.vtail)]
+             ("vcode", dc.vcode), ("vmeta", dc.vmeta), ("ktail", dc.ktail), ("vtail", dc.vtail),
+             ("vpidx", getattr(dc, "vpidx", None)), ("vprot", getattr(dc, "vprot", None))]
     for name, t in pairs:
         if t is None or name not in oc or oc[name].size == 0:
             continue
         g = host(t)
         o = oc[name]
+        if name == "vpidx":  # one little-endian word per group: the oracle keeps its four bytes
+            g, o = g.view(np.uint32), np.ascontiguousarray(o).view(np.uint32)[..., 0]
         if streams is not None:
             g = np.stack([g[b, h] for b, h in streams])
             o = np.stack([o[b, h] for b, h in streams])

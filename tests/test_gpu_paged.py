@@ -21,7 +21,7 @@ pytestmark = pytest.mark.gpu
 
 W = synth.WORKLOADS
 PER_TOKEN = ("kcode", "scode", "ssc")          # one row per token: pages hold [Hkv][32][...]
-PER_GROUP = ("kmeta", "v", "vcode", "vmeta")  # one block per group: pages hold [Hkv][...]
+PER_GROUP = ("kmeta", "v", "vcode", "vmeta", "vpidx", "vprot")  # one block per group: pages hold [Hkv][...]
 
 
 def _gathered(pc, table, G):
@@ -31,7 +31,7 @@ def _gathered(pc, table, G):
     B = idx.shape[0]
     out = SimpleNamespace(ktail=pc.ktail, vtail=pc.vtail)
     for name in PER_TOKEN + PER_GROUP:
-        t = getattr(pc, name)
+        t = getattr(pc, name, None)
         if t is None:
             setattr(out, name, None)
             continue
@@ -43,7 +43,7 @@ def _gathered(pc, table, G):
     return out
 
 
-def _run(w, B, cap, steps, out_bf16=False, n_splits=0, seed=11):
+def _run(w, B, cap, steps, out_bf16=False, n_splits=0, seed=11, value_protect=0, a_dir=None):
     import torch
     import quantized_kv_cache_headq_amd as hq
     G = cap // 32
@@ -57,12 +57,14 @@ def _run(w, B, cap, steps, out_bf16=False, n_splits=0, seed=11):
     U = orc.calibrate(synth.calibration_queries(w, n_cal=128), w.n_kv_heads, w.rank)[0] if w.rank else None
     Kf = synth.stack_streams(w, "keys", B, cap)
     Vf = synth.stack_streams(w, "values", B, cap)
-    pc = hq.PagedDeviceCache(config(w, B, cap), n_pages=n_pages, max_pages=max_pages)
+    pc = hq.PagedDeviceCache(config(w, B, cap, value_protect), n_pages=n_pages, max_pages=max_pages)
     pc.block_table.copy_(torch.from_numpy(table))
     if w.rank:
         pc.set_basis(U)
+    if value_protect:
+        pc.set_direction(a_dir)
     oc = orc.empty_cache(B, w.n_kv_heads, cap, w.head_dim, w.rank, VMODE[w.value_mode], VDT[w.value_dtype],
-                         key_dtype=VDT[w.key_dtype], base_bits=w.base_bits)
+                         key_dtype=VDT[w.key_dtype], base_bits=w.base_bits, value_protect=value_protect)
     lengths = np.array([(7 * b) % 32 for b in range(B)])  # rows start at different offsets
     for n_new in steps:
         K = np.stack([Kf[b, :, lengths[b]:lengths[b] + n_new] for b in range(B)])
@@ -73,7 +75,7 @@ def _run(w, B, cap, steps, out_bf16=False, n_splits=0, seed=11):
             for h in range(w.n_kv_heads):
                 orc.write_stream(oc, b, h, int(lengths[b]), K[b, h], value_payload(V[b, h], w),
                                  None if U is None else U[h], VMODE[w.value_mode], VDT[w.value_dtype],
-                                 bits=w.base_bits)
+                                 bits=w.base_bits, a_h=None if a_dir is None else a_dir[h])
         lengths = lengths + n_new
         compare_cache(_gathered(pc, table, G), oc)
         n_max = int(lengths.max())
@@ -92,7 +94,7 @@ def _run(w, B, cap, steps, out_bf16=False, n_splits=0, seed=11):
     owned = set(table[:, :G].ravel().tolist())
     spare = [p for p in range(n_pages) if p not in owned]
     for name in PER_TOKEN + PER_GROUP:
-        t = getattr(pc, name)
+        t = getattr(pc, name, None)
         if t is not None:
             assert int((t[spare] != 0).sum()) == 0, name
 

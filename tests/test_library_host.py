@@ -24,8 +24,8 @@ def _header_functions():
 
 def test_library_exports_every_declared_symbol():
     declared = _header_functions()
-    assert declared == sorted(["headq_calibrate", "headq_cache_append", "headq_decode_attn", "headq_prefill_attn",
-                               "headq_score_diagnostics", "headq_status_string"])
+    assert declared == sorted(["headq_calibrate", "headq_calibrate_mean", "headq_cache_append", "headq_decode_attn",
+                               "headq_prefill_attn", "headq_score_diagnostics", "headq_status_string"])
     out = subprocess.run(["nm", "-D", "--defined-only", str(bd.LIB_PATH)], capture_output=True, text=True,
                          check=True).stdout
     exported = set(re.findall(r" T (headq_\w+)", out))
@@ -256,3 +256,35 @@ def test_prefill_validation_statuses():
     assert _prefill_status(cfg, out_dtype=3) == 7
     assert _prefill_status(cfg, q=None) == 1
     assert _prefill_status(cfg, cache=_paged(cfg, 3, 8)) == 2            # paged: capacity > 32 * max_pages
+
+
+def test_calibrate_mean_matches_the_oracle_bit_for_bit():
+    """The policy's direction: the library's host mean and the oracle's take the same f64 sums in the
+    same order, so the f32 results agree exactly."""
+    w = synth.scaled(synth.WORKLOADS["qwen7b_decode"], n_q_heads=14, n_kv_heads=2)
+    q = synth.calibration_queries(w, n_cal=96)
+    cfg = hq.Config(head_dim=w.head_dim, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads, batch=1, capacity=32,
+                    rank=w.rank)
+    a = hq.headq_calibrate_mean(cfg, q)
+    assert np.array_equal(a.view(np.uint32), orc.mean_query(q, w.n_kv_heads).view(np.uint32))
+
+
+def test_value_policy_settings_are_validated():
+    w = synth.scaled(synth.WORKLOADS["qwen14b_fullkv"], n_q_heads=10, n_kv_heads=2)
+    base = dict(head_dim=w.head_dim, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads, batch=1, capacity=64,
+                rank=w.rank, value_mode=bd.HEADQ_V_Q2)
+    q = np.zeros((1, 10, 128), np.float32)
+    for bad in (dict(value_protect=3), dict(value_protect=-1), dict(value_protect=1, value_mode=bd.HEADQ_V_DENSE),
+                dict(value_protect=1, base_bits=4)):
+        cfg = hq.Config(**{**base, **bad})
+        with pytest.raises(hq.HeadQError, match="UNSUPPORTED"):
+            hq.decode_workspace_bytes(cfg, 64)
+    # the policy needs its direction, indices and corrections (checked before any GPU call)
+    cfg = hq.Config(**base, value_protect=2)
+    buf = np.zeros(64, np.uint64)  # 16-byte aligned stand-in address for every other buffer
+    addr = buf.ctypes.data
+    cache = bd.headq_cache(addr, addr, addr, addr, None, addr, addr, addr, addr, addr, None, 0, 0, None, addr, addr)
+    lib = hq.load()
+    st = lib.headq_cache_append(ctypes.byref(cfg.c()), ctypes.byref(cache), 16, (ctypes.c_int64 * 3)(1, 1, 128),
+                                None, None, 0, 32, None, None)
+    assert bd.STATUS[st] == "HEADQ_ERR_NULL"
