@@ -44,14 +44,17 @@ TRAFFIC = {
 }
 
 
-def algorithmic_bytes_per_token_head(w) -> int:
-    """Bytes the method must move per cached token per KV head (keys, side code, values)."""
+def algorithmic_bytes_per_token_head(w, value_protect: int = 0) -> float:
+    """Bytes the method must move per cached token per KV head (keys, side code, values; with the
+    A^2 value policy also each group's P bfloat16 correction rows and its index word)."""
     d, r = w.head_dim, w.rank
     k = d // 4 + d // 8 + r // 2 + (2 if r else 0)  # 2-bit codes, fp16 step/zero per 32 tokens, nibbles, sigma
     if w.value_mode == "dense":
         v = d * (4 if w.value_dtype == "f32" else 2)
     else:
         v = d // 4 + d // 8  # 2-bit codes, fp16 step/zero per 32 channels
+    if value_protect:
+        return k + v + (value_protect * d * 2 + 4) / 32
     return k + v
 
 
@@ -107,7 +110,7 @@ def traffic_per_launch(workload: str):
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(w, U, threads: int, rows: int, cpu_seconds: float = 15.0):
+def cpu_baseline(w, U, threads: int, rows: int, cpu_seconds: float = 15.0, value_protect: int = 0, a_dir=None):
     """The CPU oracle (as it stands) on a bounded sample: `rows` batch rows, all heads, full context,
     repeated for about `cpu_seconds` of CPU time."""
     from concurrent.futures import ThreadPoolExecutor
@@ -121,13 +124,13 @@ def cpu_baseline(w, U, threads: int, rows: int, cpu_seconds: float = 15.0):
     vdt = 0 if w.value_dtype == "f32" else 1
     vmode = 0 if w.value_mode == "dense" else 1
     def build(b):
-        oc = orc.empty_cache(1, w.n_kv_heads, w.n_ctx, w.head_dim, w.rank, vmode, vdt)
+        oc = orc.empty_cache(1, w.n_kv_heads, w.n_ctx, w.head_dim, w.rank, vmode, vdt, value_protect=value_protect)
         for h in range(w.n_kv_heads):
             k = synth.keys(w, b, h)
             v = synth.values(w, b, h)
             if vmode == 0 and vdt == 1:
                 v = (v.view(np.uint32) >> 16).astype(np.uint16)
-            orc.write_stream(oc, 0, h, 0, k, v, U[h], vmode, vdt)
+            orc.write_stream(oc, 0, h, 0, k, v, U[h], vmode, vdt, a_h=None if a_dir is None else a_dir[h])
         return oc
 
     with ThreadPoolExecutor(max_workers=threads) as ex:
@@ -151,17 +154,20 @@ def cpu_baseline(w, U, threads: int, rows: int, cpu_seconds: float = 15.0):
                       f"{w.n_ctx} tokens, {passes} passes ({wall:.2f} s wall, {cpu:.1f} s CPU)"}
 
 
-DIAG_WORKLOADS = {"qwen7b_diagnostics": "qwen7b_decode"}  # diagnostics step over a decode workload's cache
+# diagnostics step over a decode workload's cache
+DIAG_WORKLOADS = {"qwen7b_diagnostics": "qwen7b_decode", "qwen14b_fullkv_diagnostics": "qwen14b_fullkv"}
+DESC = {"qwen7b_decode": "Qwen2.5-7B-shaped", "qwen14b_fullkv": "Qwen2.5-14B-shaped full-KV 2-bit"}
 
 
-def diagnostics_bytes_per_token_head(w) -> int:
+def diagnostics_bytes_per_token_head(w, value_protect: int = 0) -> float:
     """Bytes the diagnostics must read per token per KV head: reference keys and values, and the
-    cache's keys (codes, step/zero, side code) and values."""
+    cache's keys (codes, step/zero, side code) and values (with the value policy's corrections)."""
     es = {"f32": 4, "bf16": 2}
-    return w.head_dim * (es[w.key_dtype] + es[w.value_dtype]) + algorithmic_bytes_per_token_head(w)
+    return w.head_dim * (es[w.key_dtype] + es[w.value_dtype]) + algorithmic_bytes_per_token_head(w, value_protect)
 
 
-def diag_cpu_baseline(w, U, K, V, q, threads: int, streams: int, cpu_seconds: float = 15.0):
+def diag_cpu_baseline(w, U, K, V, q, threads: int, streams: int, cpu_seconds: float = 15.0, value_protect: int = 0,
+                      a_dir=None):
     """The oracle's score_diagnostics (as it stands) on a bounded sample of (b, h) streams."""
     from concurrent.futures import ThreadPoolExecutor
 
@@ -175,11 +181,13 @@ def diag_cpu_baseline(w, U, K, V, q, threads: int, streams: int, cpu_seconds: fl
     pick = [(b % w.batch, b % w.n_kv_heads) for b in range(streams)]
     wb = synth.scaled(w, batch=1, n_kv_heads=1, n_q_heads=g)
 
+    vmode = 0 if w.value_mode == "dense" else 1
+
     def build(bh):
         b, h = bh
-        oc = orc.empty_cache(1, 1, w.n_ctx, w.head_dim, w.rank, 0, 1)
-        v = (np.ascontiguousarray(V[b, h]).view(np.uint32) >> 16).astype(np.uint16)
-        orc.write_stream(oc, 0, 0, 0, K[b, h], v, U[h], 0, 1)
+        oc = orc.empty_cache(1, 1, w.n_ctx, w.head_dim, w.rank, vmode, 1, value_protect=value_protect)
+        v = (np.ascontiguousarray(V[b, h]).view(np.uint32) >> 16).astype(np.uint16) if vmode == 0 else V[b, h]
+        orc.write_stream(oc, 0, 0, 0, K[b, h], v, U[h], vmode, 1, a_h=None if a_dir is None else a_dir[h])
         return oc
 
     with ThreadPoolExecutor(max_workers=threads) as ex:
@@ -188,7 +196,7 @@ def diag_cpu_baseline(w, U, K, V, q, threads: int, streams: int, cpu_seconds: fl
     def one(i):
         b, h = pick[i]
         dg.score_diagnostics(caches[i], q[b:b + 1, h * g:(h + 1) * g], U[h:h + 1], wb.n_ctx, 1.0,
-                             K[b:b + 1, h:h + 1], V[b:b + 1, h:h + 1], 0, 1)
+                             K[b:b + 1, h:h + 1], V[b:b + 1, h:h + 1], vmode, 1)
 
     passes, cpu, wall = 0, 0.0, 0.0
     with ThreadPoolExecutor(max_workers=threads) as ex:
@@ -319,11 +327,16 @@ def run_diagnostics(args, hq, synth, torch, np):
     dev = torch.device("cuda:0")
     DT = {"f32": hq.HEADQ_F32, "bf16": hq.HEADQ_BF16}
     tdt = {"f32": torch.float32, "bf16": torch.bfloat16}
+    P = args.value_protect
+    if P and w.value_mode != "q2":
+        print("bench.py: --value-protect needs a workload with 2-bit values", file=sys.stderr)
+        sys.exit(2)
     cfg = hq.Config(head_dim=w.head_dim, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads, batch=w.batch,
                     capacity=w.n_ctx, rank=w.rank, key_dtype=DT[w.key_dtype], value_dtype=DT[w.value_dtype],
                     value_mode=hq.HEADQ_V_DENSE if w.value_mode == "dense" else hq.HEADQ_V_Q2,
-                    query_dtype=DT[w.query_dtype])
-    U, _ = hq.headq_calibrate(cfg, synth.calibration_queries(w))
+                    query_dtype=DT[w.query_dtype], value_protect=P)
+    qcal = synth.calibration_queries(w)
+    U, _ = hq.headq_calibrate(cfg, qcal)
     Kh = synth.stack_streams(w, "keys", workers=16)
     Vh = synth.stack_streams(w, "values", workers=16)
     qh = synth.decode_queries(w)
@@ -332,6 +345,9 @@ def run_diagnostics(args, hq, synth, torch, np):
     q = torch.from_numpy(qh).to(dev).to(tdt[w.query_dtype])
     dc = hq.DeviceCache(cfg, device=dev)
     dc.set_basis(U)
+    a_dir = hq.headq_calibrate_mean(cfg, qcal) if P else None
+    if P:
+        dc.set_direction(a_dir)
     dc.append(K, V, 0)
     n_ctx = w.n_ctx
     nb = hq.diagnostics_workspace_bytes(cfg, n_ctx, args.splits)
@@ -358,7 +374,7 @@ def run_diagnostics(args, hq, synth, torch, np):
     wall = time.perf_counter() - t_start
     step_ms = np.array([a.elapsed_time(b) for a, b in ev])
     ms = float(step_ms.mean())
-    per_tok = diagnostics_bytes_per_token_head(w)
+    per_tok = diagnostics_bytes_per_token_head(w, P)
     alg = per_tok * w.batch * w.n_kv_heads * n_ctx
     achieved = alg / (ms / 1e3) / 1e9
     tok_heads = w.batch * w.n_q_heads * n_ctx
@@ -368,21 +384,26 @@ def run_diagnostics(args, hq, synth, torch, np):
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f64", "data": "synthetic",
         "config": {"workload": f"{args.workload}: headq_score_diagnostics (Fisher variance, KL, A^2, entropy) over "
-                               f"the Qwen2.5-7B-shaped cache, Hq {w.n_q_heads}, Hkv {w.n_kv_heads}, d {w.head_dim}, "
-                               f"batch {w.batch}, context {n_ctx}, rank {w.rank}, bf16 reference keys and values",
+                               f"the {DESC[w.name]} cache, Hq {w.n_q_heads}, Hkv {w.n_kv_heads}, d {w.head_dim}, "
+                               f"batch {w.batch}, context {n_ctx}, rank {w.rank}, bf16 reference keys and values"
+                               + (f", A^2 value policy ({P} corrected tokens per group)" if P else ""),
                    "batch": w.batch, "n_ctx": n_ctx, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
-                   "head_dim": w.head_dim, "rank": w.rank, "n_splits": args.splits or "auto",
+                   "head_dim": w.head_dim, "rank": w.rank, "n_splits": args.splits or "auto", "value_protect": P,
                    "step": "headq_score_diagnostics (query prep, value errors, stream pass, split merge)"},
         "roofline": {"bound": "hbm", "kernel": "headq_score_diagnostics (four launches, timed together)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic_per_launch(args.workload), "algorithmic_bytes_per_launch": alg,
+                     "traffic": None if P else traffic_per_launch(args.workload), "algorithmic_bytes_per_launch": alg,
                      "bytes_per_token_kv_head": per_tok,
                      "copy_ceiling_gbs": copy_gbs},
         "ms_p10_p90": [float(np.percentile(step_ms, 10)), float(np.percentile(step_ms, 90))],
         "wall_s_timed": wall,
+        # the statistics themselves, mean over (batch row, query head) of the last call
+        "stats_mean": dict(zip(hq.DIAG_STATS, np.nanmean(stats.cpu().numpy().reshape(-1, len(hq.DIAG_STATS)),
+                                                           axis=0).tolist())),
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = diag_cpu_baseline(w, U, Kh, Vh, qh, min(16, os.cpu_count() or 1), 16)
+        result["cpu_baseline"] = diag_cpu_baseline(w, U, Kh, Vh, qh, min(16, os.cpu_count() or 1), 16, value_protect=P,
+                                                   a_dir=a_dir)
     print(json.dumps(result), flush=True)
 
 
@@ -399,6 +420,8 @@ def main():
     ap.add_argument("--paged", action="store_true",
                     help="paged caches: every 32-token group in a page of shared pools, through a shuffled block table")
     ap.add_argument("--copy-probe", action="store_true", help="launch one 1 GiB device copy (counter scaling)")
+    ap.add_argument("--value-protect", type=int, default=0,
+                    help="A^2 value policy: corrected tokens per 32-token group (2-bit value workloads)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -426,16 +449,20 @@ def main():
     dev = torch.device("cuda:0")
     w = synth.WORKLOADS[args.workload]
     DT = {"f32": hq.HEADQ_F32, "bf16": hq.HEADQ_BF16}
+    if args.value_protect and w.value_mode != "q2":
+        print("bench.py: --value-protect needs a workload with 2-bit values", file=sys.stderr)
+        sys.exit(2)
     cfg = hq.Config(head_dim=w.head_dim, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads, batch=w.batch,
                     capacity=w.n_ctx, rank=w.rank, key_dtype=DT[w.key_dtype], value_dtype=DT[w.value_dtype],
                     value_mode=hq.HEADQ_V_DENSE if w.value_mode == "dense" else hq.HEADQ_V_Q2,
-                    query_dtype=DT[w.query_dtype])
+                    query_dtype=DT[w.query_dtype], value_protect=args.value_protect)
     tdt = {"f32": torch.float32, "bf16": torch.bfloat16}
 
     # ---- inputs (seeded, synthetic), offline calibration
     qcal = synth.calibration_queries(w)
     t0 = time.perf_counter()
     U, _ = hq.headq_calibrate(cfg, qcal)
+    a_dir = hq.headq_calibrate_mean(cfg, qcal) if args.value_protect else None
     calib_s = time.perf_counter() - t0
     append_only = w.name == "append_prefill"
     K = torch.from_numpy(synth.stack_streams(w, "keys", workers=16)).to(dev).to(tdt[w.key_dtype])
@@ -454,6 +481,8 @@ def main():
         else:
             dc = hq.DeviceCache(cfg, device=dev)
         dc.set_basis(U)
+        if args.value_protect:
+            dc.set_direction(a_dir)
         dc.append(K, V, 0)
         caches.append(dc)
     n_ctx = w.n_ctx
@@ -534,12 +563,14 @@ def main():
                     f"context {n_ctx}, 2-bit keys + rank-{w.rank} 4-bit side code"
                     + ("" if append_only else f", {w.value_mode} {kinds[w.value_dtype]} values")
                     + (f", {n_layers} layers" if n_layers > 1 else "")
-                    + (", paged (shuffled 32-token pages)" if args.paged else ""),
+                    + (", paged (shuffled 32-token pages)" if args.paged else "")
+                    + (f", A^2 value policy ({args.value_protect} corrected tokens per group)"
+                       if args.value_protect else ""),
         "batch": w.batch, "n_ctx": n_ctx, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
         "head_dim": w.head_dim, "rank": w.rank, "layers": n_layers,
         "step": ("headq_cache_append of the whole prefill (keys)" if append_only else
                  "per layer: append newest 32-token group + decode over the full context"),
-        "cache_copies": len(caches), "n_splits": args.splits or "auto", "paged": bool(args.paged),
+        "cache_copies": len(caches), "n_splits": args.splits or "auto", "paged": bool(args.paged), "value_protect": args.value_protect,
     }
     result = {
         "metric": METRIC,
@@ -574,12 +605,13 @@ def main():
         })
     else:
         tok_heads = w.batch * w.n_q_heads * n_ctx * n_layers
-        per_tok = algorithmic_bytes_per_token_head(w)
+        per_tok = algorithmic_bytes_per_token_head(w, args.value_protect)
         alg_bytes = per_tok * w.batch * w.n_kv_heads * n_ctx
         dec_s = float(decode_ms.mean()) / 1e3
         achieved = alg_bytes / dec_s / 1e9
         mfma = w.value_mode == "q2" or w.value_dtype == "bf16"
-        traffic = None if args.paged else traffic_per_launch(w.name)  # counters were taken on contiguous caches
+        # counters were taken on contiguous caches without the value policy
+        traffic = None if args.paged or args.value_protect else traffic_per_launch(w.name)
         result.update({
             "value": tok_heads / (ms_per_step / 1e3),
             "unit": "query-head cached tokens/s",
@@ -603,7 +635,8 @@ def main():
     result["wall_s_timed"] = wall
     if not args.no_cpu_baseline and not append_only:
         threads = min(16, os.cpu_count() or 1)
-        result["cpu_baseline"] = cpu_baseline(w, U, threads, min(args.cpu_rows, w.batch))
+        result["cpu_baseline"] = cpu_baseline(w, U, threads, min(args.cpu_rows, w.batch), value_protect=args.value_protect,
+                                              a_dir=a_dir)
     print(json.dumps(result), flush=True)
 
 

@@ -184,9 +184,9 @@ headq_status headq_calibrate_mean(const headq_config* cfg, const float* q_cal, i
  *   sigma = fp16(max_i |y_i| / 7), zc_i = clamp(rint(y_i * (1/sigma)), -7, 7) (all 0 if sigma == 0)
  * Dense values are copied into the cache layout; 2-bit values get the per-token quantizer over
  * 32-channel groups with the same numerics, and with value_protect > 0 every encoded group gets
- * the A^2 value policy's corrections (headq_calibrate_mean; its direction from cache->vdir). Appends may be token-granular: every 32-token group
- * that is whole once tokens [start, start + n_new) are in is encoded (its tokens before `start`
- * are taken from the tails), and the tokens of an unfinished last group are copied exactly into
+ * the A^2 value policy's corrections (headq_calibrate_mean; its direction from cache->vdir).
+ * Appends may be token-granular: every 32-token group that is whole once tokens
+ * [start, start + n_new) are in is encoded (its tokens before `start` are taken from the tails), and the tokens of an unfinished last group are copied exactly into
  * ktail / vtail (rows t % 32). Appends to a stream must be sequential: the tails hold tokens
  * [32 * floor(start / 32), start) from earlier calls.
  *   k        device keys, key_dtype, element (b, h, t, c) at k[b*ks[0] + h*ks[1] + t*ks[2] + c]
@@ -229,6 +229,8 @@ headq_status headq_cache_append(const headq_config* cfg, const headq_cache* cach
  *               the size of ws. The workspace must be zero-filled before its first use; every
  *               call leaves its leading counter region zero again, so one zeroed workspace
  *               serves any number of calls. Calls that share a workspace must not overlap.
+ * With value_protect > 0 the readout adds p_t * correction_t for every token t the cache holds
+ * a correction for (the matrix-core kernel; HEADQ_DECODE_KERNEL=valu then returns UNSUPPORTED).
  * Errors: NULL (also: n_ctx % 32 != 0 without both tails), SHAPE, ALIGN, CAPACITY, WORKSPACE,
  * UNSUPPORTED, HIP.
  */
@@ -252,7 +254,7 @@ headq_status headq_decode_attn(const headq_config* cfg, const headq_cache* cache
  *   logits_dbg  device f32 [B][n_q][Hq][start + n_q]: logits of the attended tokens (natural-log
  *               units; entries past a token's causal limit are left untouched), or NULL
  * Errors: NULL (also: start + n_q not a multiple of 32 without both tails), SHAPE, ALIGN,
- * CAPACITY, UNSUPPORTED, HIP.
+ * CAPACITY, UNSUPPORTED (also: value_protect > 0), HIP.
  */
 headq_status headq_prefill_attn(const headq_config* cfg, const headq_cache* cache, const void* q, int64_t start,
                                 int64_t n_q, void* out, int32_t out_dtype, float corr_scale, float* logits_dbg,
@@ -277,8 +279,9 @@ enum {
  * perturbed attention is its Fisher-weighted variance; §2.2: the A^2 surrogate weighs each
  * token's value distortion by p_j^2. Here s_j = q.k_j/sqrt(d) from the reference keys,
  * p = softmax(s), s_hat_j the cache's corrected logit of §3 step 3 (base key plus corr_scale
- * times the side correction; tokens in the tails are exact), v_hat_j the cache's value. All
- * arithmetic is f64; KL is evaluated as log E_p[exp(ds)] - E_p[ds].
+ * times the side correction; tokens in the tails are exact), v_hat_j the cache's value (with the
+ * A^2 value policy's correction where the cache holds one). All arithmetic is f64; KL is
+ * evaluated as log E_p[exp(ds)] - E_p[ds].
  *   q        device [B][Hq][d] in query_dtype (contiguous)
  *   k_ref    device reference keys in key_dtype, element (b, h, t, c) at
  *            k_ref[b*ks[0] + h*ks[1] + t*ks[2] + c] (as for headq_cache_append)

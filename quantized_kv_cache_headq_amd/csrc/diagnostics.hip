@@ -147,6 +147,7 @@ __global__ __launch_bounds__(kThreads) void diag_value_kernel(DiagArgs a) {
   __shared__ float val_s[D][PV];              // the cache's values [c][t] (dense or tail)
   __shared__ __attribute__((aligned(16))) uint8_t code_s[D * 8];  // 2-bit: the code block as stored
   __shared__ __attribute__((aligned(16))) uint16_t meta_s[2 * D];  // 2-bit: step, zero [2][d/32][32]
+  __shared__ __attribute__((aligned(16))) uint16_t prot_s[2 * D];  // the value policy's corrections [P][d]
   __shared__ double part_s[8][kGroup];
   const int h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
   const int64_t g0 = (int64_t)blockIdx.x * kGroup;
@@ -198,12 +199,23 @@ __global__ __launch_bounds__(kThreads) void diag_value_kernel(DiagArgs a) {
         reinterpret_cast<uint4*>(code_s)[i] = reinterpret_cast<const uint4*>(a.vcode + blk * D * 8)[i];
       for (int i = tid; i < 2 * D / 8; i += kThreads)
         reinterpret_cast<uint4*>(meta_s)[i] = reinterpret_cast<const uint4*>(a.vmeta + blk * 2 * D)[i];
+      for (int i = tid; i < a.value_protect * D / 8; i += kThreads)
+        reinterpret_cast<uint4*>(prot_s)[i] =
+            reinterpret_cast<const uint4*>(a.vprot + blk * a.value_protect * D)[i];
     }
   }
+  // the group's corrected tokens (A^2 value policy): the cache's value of token t is then
+  // code * s + z + correction
+  uint32_t pidx = 0;
+  if (!tail && a.value_mode != HEADQ_V_DENSE && a.value_protect)
+    pidx = a.vpidx[a.map.block(b, h, g0 / kGroup)];
   __syncthreads();
 
   const int t = tid % kGroup, part = tid / kGroup;
   const bool q2 = !tail && a.value_mode != HEADQ_V_DENSE;
+  int pslot = -1;  // this token's correction slot, if any
+  for (int k = 0; k < (q2 ? a.value_protect : 0); ++k)
+    if ((int)((pidx >> (8 * k)) & 31u) == t) pslot = k;
   double e2 = 0.0;
   if (t < n_tok) {
     const int bit = vcode_pair_bit(t);
@@ -216,6 +228,7 @@ __global__ __launch_bounds__(kThreads) void diag_value_kernel(DiagArgs a) {
         const int gc = c / 32;
         vh = (double)((pair >> bit) & 3u) * f16_bits(meta_s[gc * kGroup + t]) +
              f16_bits(meta_s[(D / 32 + gc) * kGroup + t]);
+        if (pslot >= 0) vh += bf16_bits(prot_s[pslot * D + c]);
       } else {
         vh = (double)val_s[c][t];
       }

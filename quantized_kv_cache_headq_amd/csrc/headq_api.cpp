@@ -297,7 +297,6 @@ extern "C" headq_status headq_score_diagnostics(const headq_config* cfg, const h
   headq_status st = check_config(cfg);
   if (st != HEADQ_OK) return st;
   if (!ws_bytes) return HEADQ_ERR_NULL;
-  if (cfg->value_protect) return HEADQ_ERR_UNSUPPORTED;  // the A^2 value policy is read by the decode only
   if (n_ctx < 1) return HEADQ_ERR_SHAPE;
   if (n_ctx > cfg->capacity) return HEADQ_ERR_CAPACITY;
   const int64_t n_chunks = (n_ctx + 63) / 64;  // 64-token chunks, one wave each at a time
@@ -369,6 +368,9 @@ extern "C" headq_status headq_score_diagnostics(const headq_config* cfg, const h
   a.U = cache->U;
   a.ktail = cache->ktail;
   a.vtail = cache->vtail;
+  a.value_protect = cfg->value_protect;
+  a.vpidx = cache->vpidx;
+  a.vprot = cache->vprot;
   a.map = map_of(cfg, cache);
   const int g = a.gqa;
   a.ws_q = (double*)ws;

@@ -143,6 +143,9 @@ struct DiagArgs {
   const float* U;
   const void* ktail;
   const void* vtail;
+  const uint32_t* vpidx;       // A^2 value policy (value_protect > 0): indices per group block
+  const uint16_t* vprot;       //   and [P][d] bf16 corrections per group block
+  int value_protect;
   CacheMap map;
   double* ws_q;                // [B][Hkv][padded g][d]   queries in f64 (zero rows past g)
   double* ws_qu;               // [B][Hkv][padded g][max(r, 1)]   U_h^T q in f64

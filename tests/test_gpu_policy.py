@@ -5,8 +5,8 @@ bit for bit (a discrete decision both sides take in the same f32/f64 arithmetic)
 which adds p_t * correction_t for the chosen tokens, must meet the decode tolerances against the
 oracle's fp64 decode of its own cache. Cases: one and two corrected tokens, d = 64 and 128, one
 group per matrix product (g = 16) and two groups sharing the columns (g <= 8), dense tails, splits,
-the two-groups-per-workgroup append of long writes, paged caches; the calls that do not read the
-corrections reject such caches.
+the two-groups-per-workgroup append of long writes, paged caches; the score-space diagnostics
+(A^2 with the corrections); the chunked prefill rejects such caches.
 """
 import numpy as np
 import pytest
@@ -93,7 +93,7 @@ def test_paged_ragged_rows():
     _run(w, 3, 160, (40, 1, 30, 33, 2), out_bf16=True, value_protect=2, a_dir=_direction(w))
 
 
-def test_prefill_and_diagnostics_reject_policy_caches():
+def test_prefill_rejects_policy_caches():
     import torch
     import quantized_kv_cache_headq_amd as hq
     w = synth.scaled(W["qwen14b_fullkv"], n_q_heads=10, n_kv_heads=2)
@@ -102,5 +102,34 @@ def test_prefill_and_diagnostics_reject_policy_caches():
     q = torch.zeros((1, 4, w.n_q_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(hq.HeadQError, match="UNSUPPORTED"):
         dc.prefill(q, 60)
-    with pytest.raises(hq.HeadQError, match="UNSUPPORTED"):
-        dc.score_diagnostics(q[:, 0], to_device(K, w.key_dtype), to_device(V, w.value_dtype), 64)
+
+
+@pytest.mark.parametrize("P", [0, 2])
+def test_diagnostics_a2_with_corrections(P):
+    """The score-space diagnostics read the corrections: every statistic against the oracle's
+    (whose value rows carry them), and A^2 falls when the policy is on."""
+    from .test_gpu_diagnostics import check_stats
+    from oracle import diagnostics as dg
+    w = synth.scaled(W["qwen14b_fullkv"], n_q_heads=10, n_kv_heads=2)
+    B, T = 2, 200
+    say("policy-diagnostics", w.name, f"P={P} B={B} T={T}")
+    U = orc.calibrate(synth.calibration_queries(w, n_cal=128), w.n_kv_heads, w.rank)[0]
+    a = _direction(w)
+    pieces = [(0, 192), (192, 8)]
+    dc, K, V = gpu_cache(w, U, B, T, 224, pieces=pieces, value_protect=P, a_dir=a)
+    oc = orc.empty_cache(B, w.n_kv_heads, 224, w.head_dim, w.rank, 1, VDT[w.value_dtype],
+                         key_dtype=VDT[w.key_dtype], value_protect=P)
+    for b in range(B):
+        for h in range(w.n_kv_heads):
+            for st, n in pieces:
+                orc.write_stream(oc, b, h, st, K[b, h, st:st + n], value_payload(V[b, h, st:st + n], w), U[h], 1,
+                                 VDT[w.value_dtype], a_h=a[h])
+    q = synth.decode_queries(w, position=T, batch=B)
+    got = dc.score_diagnostics(to_device(q, w.query_dtype), to_device(K, w.key_dtype), to_device(V, w.value_dtype),
+                               T).cpu().numpy()
+    ref = dg.score_diagnostics(oc, q, U, T, 1.0, K, V, 1, VDT[w.value_dtype])
+    check_stats(got, ref)
+    if P:
+        plain = {k: v for k, v in oc.items() if k not in ("vpidx", "vprot")}
+        ref0 = dg.score_diagnostics(plain, q, U, T, 1.0, K, V, 1, VDT[w.value_dtype])
+        assert np.mean(ref[..., 4]) < np.mean(ref0[..., 4])
