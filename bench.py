@@ -40,6 +40,7 @@ TRAFFIC = {
     "tinyllama_decode": ("decode_tinyllama_traffic.json", "decode_mfma.hip"),
     "append_prefill": ("append_prefill_traffic.json", "append.hip"),
     "qwen7b_diagnostics": ("diagnostics_qwen7b_traffic.json", "diagnostics.hip"),
+    "qwen14b_fullkv_diagnostics": ("diagnostics_qwen14b_fullkv_traffic.json", "diagnostics.hip"),
     "qwen7b_prefill": ("prefill_qwen7b_traffic.json", "prefill_mfma.hip"),
 }
 
