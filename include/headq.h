@@ -12,8 +12,10 @@
  *   read       s_j = q.k_base_j / sqrt(d) + (U_h^T q).z_hat_j / sqrt(d), softmax, sum_j p_j v_j
  *                                                                                   (§3 step 3)
  *
- * Three calls, one per phase: headq_calibrate (host), headq_cache_append (GPU),
- * headq_decode_attn (GPU).
+ * One call per phase: headq_calibrate (host), headq_cache_append (GPU), headq_decode_attn (GPU);
+ * around them headq_prefill_attn (chunked-prefill attention, GPU), headq_score_diagnostics
+ * (score-space diagnostics, GPU) and headq_calibrate_mean (the direction of the optional A^2 value
+ * policy, host).
  *
  * Conventions
  *   Ownership  The caller owns every buffer. The library never allocates, frees or keeps device

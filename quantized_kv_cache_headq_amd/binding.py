@@ -1,6 +1,7 @@
 """Thin Python binding of libheadq (ctypes): argument marshalling only.
 
-The three calls keep the C names: headq_calibrate, headq_cache_append, headq_decode_attn.
+Every call keeps its C name: headq_calibrate, headq_calibrate_mean, headq_cache_append,
+headq_decode_attn, headq_prefill_attn, headq_score_diagnostics.
 PyTorch provides device memory and the current HIP stream; every step of the hot path runs in
 libheadq's HIP kernels. There is no fallback: if libheadq.so is missing or fails to load, every
 call raises.
@@ -131,7 +132,7 @@ def _stream(stream) -> int | None:
 
 
 # ------------------------------------------------------------------------------------------------
-# the three calls
+# the calls
 
 def headq_calibrate(cfg: Config, q_cal: np.ndarray):
     """Host PCA. q_cal: f32 [Hq][n_cal][d] (numpy). Returns (U f32 [Hkv][d][r], eig f64 [Hkv][r])."""
