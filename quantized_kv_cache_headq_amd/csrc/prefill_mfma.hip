@@ -48,23 +48,33 @@ struct Tile {
   static_assert(BYTES % 16 == 0 && OFF_V % 16 == 0, "16-byte staging");
 };
 
-// Source of the i-th 16-byte chunk of group gi of stream (b, h).
+// Staging plan of a group: every array of the group's block is fetched in pieces of 64 16-byte
+// chunks, one piece per wave instruction, so a piece never mixes arrays and its source is one
+// wave-uniform buffer resource (a lane's offset is its chunk). Piece q of the group (in array
+// order) goes to wave q % 4, into its register q / 4. Arrays: key codes, key step/zero, side
+// codes, sigma, 2-bit value step/zero, values.
 template <int D, int R, bool VQ2, bool NB>
-__device__ __forceinline__ const u32x4* chunk_src(const PrefillArgs& a, int64_t blk, int i) {
+struct Stage {
   using TL = Tile<D, R, VQ2, NB>;
-  int off = 16 * i;
-  if (off < TL::KC) return reinterpret_cast<const u32x4*>(a.kcode + blk * TL::KC + off);
-  off -= TL::KC;
-  if (off < TL::KM) return reinterpret_cast<const u32x4*>((const char*)a.kmeta + blk * TL::KM + off);
-  off -= TL::KM;
-  if (off < TL::SC) return reinterpret_cast<const u32x4*>(a.scode + blk * TL::SC + off);
-  off -= TL::SC;
-  if (off < TL::SG) return reinterpret_cast<const u32x4*>((const char*)a.ssc + blk * TL::SG + off);
-  off -= TL::SG;
-  if (off < TL::VM) return reinterpret_cast<const u32x4*>((const char*)a.vmeta + blk * TL::VM + off);
-  off -= TL::VM;
-  const char* vb = VQ2 ? (const char*)a.vcode : (const char*)a.vdense;
-  return reinterpret_cast<const u32x4*>(vb + blk * TL::VB + off);
+  static constexpr int NARR = 6;
+  static constexpr int BYTES[NARR] = {TL::KC, TL::KM, TL::SC, TL::SG, TL::VM, TL::VB};
+  static constexpr int OFF[NARR] = {0, TL::OFF_KM, TL::OFF_SC, TL::OFF_SG, TL::OFF_VM, TL::OFF_V};
+  static constexpr int chunks(int A) { return BYTES[A] / 16; }
+  static constexpr int pieces(int A) { return (chunks(A) + 63) / 64; }
+  static constexpr int first(int A) {
+    int q = 0;
+    for (int i = 0; i < A; ++i) q += pieces(i);
+    return q;
+  }
+  static constexpr int KV = (first(NARR) + 3) / 4;  // pieces (16-byte registers) per lane
+  static_assert(TL::KC % 16 == 0 && TL::KM % 16 == 0 && TL::SC % 16 == 0 && TL::SG % 16 == 0 &&
+                    TL::VM % 16 == 0 && TL::VB % 16 == 0,
+                "16-byte chunks");
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t stage_rsrc(const void* base, int64_t bytes) {
+  const uint32_t nbytes = bytes > 0x7fffffff ? 0x7fffffffu : (uint32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes, 0x00020000);
 }
 
 // Per-lane operands fixed for the whole kernel (column n of the wave).
@@ -355,7 +365,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
   using TL = Tile<D, R, VQ2, NB>;
   constexpr int RU = R > 0 ? R : 1;
   constexpr int NKT = D / 32, NCT = D / 16, NG = D / 32;
-  constexpr int NPF = (TL::CHUNKS + kThreads - 1) / kThreads;  // staged chunks per thread
+  using ST = Stage<D, R, VQ2, NB>;
   __shared__ u32x4 tile_s[2][TL::CHUNKS];
   __shared__ float qs[kCols][D];        // scaled queries of the workgroup's columns
   __shared__ float qu_s[kCols][RU];     // U^T q (scaled)
@@ -457,37 +467,92 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
   float m_run = -INFINITY, l_run = 0.0f;
 
   // ---- the stream's whole groups, staged by the workgroup (double-buffered)
-  u32x4 pf[NPF];
-  auto fetch_group = [&](int64_t gi) {
-    const int64_t blk = a.map.block(b, h, gi);
-#pragma unroll
-    for (int k = 0; k < NPF; ++k) {
-      const int i = tid + k * kThreads;
-      if (i < TL::CHUNKS) pf[k] = *chunk_src<D, R, VQ2, NB>(a, blk, i);
+  // groups in flight in registers: a ring of PD sets, so a group's loads have PD - 1 group steps
+  // to arrive before it is staged
+  constexpr int PD = 3;
+  u32x4 pf[PD][ST::KV];
+  // the arrays of this stream: byte base and size of the region the group offsets index
+  const int64_t groups_cap = a.cap / kGroup;
+  auto arr_base = [&](int i) -> const char* {  // i is a compile-time constant at every use
+    switch (i) {
+      case 0: return (const char*)a.kcode;
+      case 1: return (const char*)a.kmeta;
+      case 2: return (const char*)a.scode;
+      case 3: return (const char*)a.ssc;
+      case 4: return (const char*)a.vmeta;
+      default: return VQ2 ? (const char*)a.vcode : (const char*)a.vdense;
     }
   };
-  auto stage_group = [&](int buf) {
+  // piece 4 * j + wave of a group: its array A (wave-uniform, by scalar compares) and chunk
+  auto piece_array = [&](int q) {
+    int A = 0;
 #pragma unroll
-    for (int k = 0; k < NPF; ++k) {
-      const int i = tid + k * kThreads;
-      if (i < TL::CHUNKS) tile_s[buf][i] = pf[k];
+    for (int i = 1; i < ST::NARR; ++i) A = (ST::pieces(i) > 0 && q >= ST::first(i)) ? i : A;
+    return A;
+  };
+  auto fetch_into = [&](u32x4* dst, int64_t gi) {
+    // contiguous caches: one resource per stream and array, the group by offset; paged caches:
+    // the group's block (page * Hkv + h) as its own resource
+    const bool paged = a.map.block_table != nullptr;
+    const int64_t blk = paged ? a.map.block(b, h, gi) : bh * groups_cap;
+#pragma unroll
+    for (int j = 0; j < ST::KV; ++j) {
+      const int q = 4 * j + wave, A = piece_array(q);
+      const char* base = arr_base(0);
+      int bytes = ST::BYTES[0], first = 0;
+#pragma unroll
+      for (int i = 1; i < ST::NARR; ++i)
+        if (A == i) {
+          base = arr_base(i);
+          bytes = ST::BYTES[i];
+          first = ST::first(i);
+        }
+      const __amdgpu_buffer_rsrc_t rs = stage_rsrc(base + blk * bytes, paged ? bytes : groups_cap * bytes);
+      const int soff = __builtin_amdgcn_readfirstlane(paged ? 0 : (int)(gi * bytes));
+      // every lane loads (a chunk past the array's end, or a piece past the group's, reads beyond
+      // the group and is not staged), so each step issues the same loads and its waits count exactly
+      dst[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * (64 * (q - first) + lane), soff, 0);
     }
   };
+  auto stage_from = [&](const u32x4* src, int buf) {
+#pragma unroll
+    for (int j = 0; j < ST::KV; ++j) {
+      const int q = 4 * j + wave, A = piece_array(q);
+      int off = ST::OFF[0], chunks = ST::chunks(0), first = 0;
+#pragma unroll
+      for (int i = 1; i < ST::NARR; ++i)
+        if (A == i) {
+          off = ST::OFF[i];
+          chunks = ST::chunks(i);
+          first = ST::first(i);
+        }
+      const int chunk = 64 * (q - first) + lane;
+      if (q < ST::first(ST::NARR) && chunk < chunks) tile_s[buf][off / 16 + chunk] = src[j];
+    }
+  };
+  // Requests are unconditional (indices past the last group read the last group again, unused),
+  // so every step issues the same loads in the same order and each wait counts exactly.
+  auto clamp_g = [&](int64_t x) { return x < G ? x : G - 1; };
   if (G > 0) {
-    fetch_group(0);
-    stage_group(0);
+#pragma unroll
+    for (int k = 0; k < PD; ++k) fetch_into(pf[k], clamp_g(k));
+    stage_from(pf[0], 0);
   }
   __syncthreads();
-  for (int64_t gi = 0; gi < G; ++gi) {
-    const int cur = (int)(gi & 1);
-    if (gi + 1 < G) fetch_group(gi + 1);  // in flight while this group is computed
-    const int64_t tok0 = gi * kGroup;
-    if (tok0 < att_max_w)
-      group_step<D, R, VQ2, NB>(reinterpret_cast<const uint8_t*>(tile_s[cur]), f, a.corr_scale, (int)tok0,
-                            tok0 + kGroup > att_min_w, (int)n_att, lg_row, n, quad, lane, o_acc, z_acc, m_run,
-                            l_run);
-    if (gi + 1 < G) stage_group(cur ^ 1);
-    __syncthreads();
+  for (int64_t g0 = 0; g0 < G; g0 += PD) {
+#pragma unroll
+    for (int k = 0; k < PD; ++k) {
+      const int64_t gi = g0 + k;
+      if (gi >= G) break;
+      fetch_into(pf[k], clamp_g(gi + PD));  // set k held group gi, staged in the step before
+      const int64_t tok0 = gi * kGroup;
+      if (tok0 < att_max_w)
+        group_step<D, R, VQ2, NB>(reinterpret_cast<const uint8_t*>(tile_s[gi & 1]), f, a.corr_scale, (int)tok0,
+                                  tok0 + kGroup > att_min_w, (int)n_att, lg_row, n, quad, lane, o_acc, z_acc, m_run,
+                                  l_run);
+      stage_from(pf[(k + 1) % PD], (int)((gi + 1) & 1));  // group gi + 1 (past the end: unused)
+      __syncthreads();
+    }
   }
 
   // ---- the cache's unfinished group, for the columns that reach it
