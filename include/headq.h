@@ -256,7 +256,8 @@ headq_status headq_decode_attn(const headq_config* cfg, const headq_cache* cache
  *   logits_dbg  device f32 [B][n_q][Hq][start + n_q]: logits of the attended tokens (natural-log
  *               units; entries past a token's causal limit are left untouched), or NULL
  * Errors: NULL (also: start + n_q not a multiple of 32 without both tails), SHAPE, ALIGN,
- * CAPACITY, UNSUPPORTED (also: value_protect > 0), HIP.
+ * CAPACITY, UNSUPPORTED, HIP. With value_protect > 0 the readout adds the A^2 value policy's
+ * corrections as the decode does.
  */
 headq_status headq_prefill_attn(const headq_config* cfg, const headq_cache* cache, const void* q, int64_t start,
                                 int64_t n_q, void* out, int32_t out_dtype, float corr_scale, float* logits_dbg,

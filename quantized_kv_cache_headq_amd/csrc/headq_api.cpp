@@ -395,7 +395,6 @@ extern "C" headq_status headq_prefill_attn(const headq_config* cfg, const headq_
   if (out_dtype != HEADQ_F32 && out_dtype != HEADQ_BF16) return HEADQ_ERR_UNSUPPORTED;
   // the matrix-core formats: dense bf16 or 2-bit values
   if (cfg->value_mode == HEADQ_V_DENSE && cfg->value_dtype != HEADQ_BF16) return HEADQ_ERR_UNSUPPORTED;
-  if (cfg->value_protect) return HEADQ_ERR_UNSUPPORTED;  // the A^2 value policy is read by the decode only
   if ((start + n_q) % headq::kGroup && (!cache->ktail || !cache->vtail)) return HEADQ_ERR_NULL;
   if (!aligned16(q) || !aligned16(out) || (logits_dbg && !aligned16(logits_dbg))) return HEADQ_ERR_ALIGN;
 
@@ -427,6 +426,9 @@ extern "C" headq_status headq_prefill_attn(const headq_config* cfg, const headq_
   a.U = cache->U;
   a.ktail = cache->ktail;
   a.vtail = cache->vtail;
+  a.value_protect = cfg->value_protect;
+  a.vpidx = cache->vpidx;
+  a.vprot = cache->vprot;
   a.map = map_of(cfg, cache);
   a.logits_dbg = logits_dbg;
   a.out = out;

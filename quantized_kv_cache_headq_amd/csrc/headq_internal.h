@@ -192,6 +192,9 @@ struct PrefillArgs {
   const float* U;
   const void* ktail;
   const void* vtail;
+  const uint32_t* vpidx;       // A^2 value policy (value_protect > 0): indices per group block
+  const uint16_t* vprot;       //   and [P][d] bf16 corrections per group block
+  int value_protect;
   CacheMap map;
   float* logits_dbg;           // [B][n_q][Hq][start + n_q] or null
   void* out;                   // [B][n_q][Hq][d]

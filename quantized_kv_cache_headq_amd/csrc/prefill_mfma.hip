@@ -38,12 +38,13 @@ constexpr float kLazyMax = 8.0f;          // rescale only when the max grows by 
 // the cache): packed key codes 32 x d/4 | key step/zero rows 2 x d x 2 | side codes 32 x r/2 |
 // sigma 32 x 2 | (2-bit values) value step/zero rows 2 x d/32 x 32 x 2 | values (dense bf16
 // [d][32], or 2-bit codes d x 8 in matrix-operand order).
-template <int D, int R, bool VQ2, bool NB>
+template <int D, int R, bool VQ2, bool NB, int VP = 0>
 struct Tile {
   static constexpr int KC = kGroup * D / (NB ? 2 : 4), KM = 4 * D, SC = kGroup * R / 2, SG = R > 0 ? kGroup * 2 : 0;
   static constexpr int VM = VQ2 ? 4 * D : 0, VB = VQ2 ? D * 8 : D * kGroup * 2;
+  static constexpr int VPB = VP * D * 2, VIB = VP > 0 ? 16 : 0;  // A^2 value policy: corrections, index word
   static constexpr int OFF_KM = KC, OFF_SC = OFF_KM + KM, OFF_SG = OFF_SC + SC, OFF_VM = OFF_SG + SG;
-  static constexpr int OFF_V = OFF_VM + VM, BYTES = OFF_V + VB;
+  static constexpr int OFF_V = OFF_VM + VM, OFF_VP = OFF_V + VB, OFF_VI = OFF_VP + VPB, BYTES = OFF_VI + VIB;
   static constexpr int CHUNKS = BYTES / 16;
   static_assert(BYTES % 16 == 0 && OFF_V % 16 == 0, "16-byte staging");
 };
@@ -52,13 +53,14 @@ struct Tile {
 // chunks, one piece per wave instruction, so a piece never mixes arrays and its source is one
 // wave-uniform buffer resource (a lane's offset is its chunk). Piece q of the group (in array
 // order) goes to wave q % 4, into its register q / 4. Arrays: key codes, key step/zero, side
-// codes, sigma, 2-bit value step/zero, values.
-template <int D, int R, bool VQ2, bool NB>
+// codes, sigma, 2-bit value step/zero, values, the value policy's corrections (its index word,
+// 4 bytes per group, is loaded on its own).
+template <int D, int R, bool VQ2, bool NB, int VP>
 struct Stage {
-  using TL = Tile<D, R, VQ2, NB>;
-  static constexpr int NARR = 6;
-  static constexpr int BYTES[NARR] = {TL::KC, TL::KM, TL::SC, TL::SG, TL::VM, TL::VB};
-  static constexpr int OFF[NARR] = {0, TL::OFF_KM, TL::OFF_SC, TL::OFF_SG, TL::OFF_VM, TL::OFF_V};
+  using TL = Tile<D, R, VQ2, NB, VP>;
+  static constexpr int NARR = 7;
+  static constexpr int BYTES[NARR] = {TL::KC, TL::KM, TL::SC, TL::SG, TL::VM, TL::VB, TL::VPB};
+  static constexpr int OFF[NARR] = {0, TL::OFF_KM, TL::OFF_SC, TL::OFF_SG, TL::OFF_VM, TL::OFF_V, TL::OFF_VP};
   static constexpr int chunks(int A) { return BYTES[A] / 16; }
   static constexpr int pieces(int A) { return (chunks(A) + 63) / 64; }
   static constexpr int first(int A) {
@@ -68,7 +70,7 @@ struct Stage {
   }
   static constexpr int KV = (first(NARR) + 3) / 4;  // pieces (16-byte registers) per lane
   static_assert(TL::KC % 16 == 0 && TL::KM % 16 == 0 && TL::SC % 16 == 0 && TL::SG % 16 == 0 &&
-                    TL::VM % 16 == 0 && TL::VB % 16 == 0,
+                    TL::VM % 16 == 0 && TL::VB % 16 == 0 && TL::VPB % 16 == 0,
                 "16-byte chunks");
 };
 
@@ -87,12 +89,39 @@ struct Fixed {
   float inv_scale;                 // 2^e: undoes the per-column query scale
 };
 
-// One staged group against the wave's 16 columns: scores, causal mask, online softmax, P.V.
-template <int D, int R, bool VQ2, bool NB>
+// o += p_t * correction_t for the group's corrected tokens t (A^2 value policy; rows at `prow`,
+// [VP][d] bf16): token t's probability for this column is held by the lane of the same column
+// with quad t / 8, slot t % 8.
+template <int D, int VP>
+__device__ __forceinline__ void add_corrections(const uint8_t* prow, uint32_t idx, const float* p, int n, int quad,
+                                                floatx4* o_acc) {
+  constexpr int NCT = D / 16;
+#pragma unroll
+  for (int k = 0; k < VP; ++k) {
+    const int t = (idx >> (8 * k)) & 31;
+    float pt = p[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) pt = (t & 7) == j ? p[j] : pt;
+    pt = __shfl(pt, n + 16 * (t >> 3));
+    const uint16_t* row = reinterpret_cast<const uint16_t*>(prow + k * D * 2);
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const u32x2 w = *reinterpret_cast<const u32x2*>(row + 16 * ct + 4 * quad);  // channels 16ct + 4quad ..+3
+      o_acc[ct][0] = fmaf(pt, __uint_as_float(w[0] << 16), o_acc[ct][0]);
+      o_acc[ct][1] = fmaf(pt, __uint_as_float(w[0] & 0xffff0000u), o_acc[ct][1]);
+      o_acc[ct][2] = fmaf(pt, __uint_as_float(w[1] << 16), o_acc[ct][2]);
+      o_acc[ct][3] = fmaf(pt, __uint_as_float(w[1] & 0xffff0000u), o_acc[ct][3]);
+    }
+  }
+}
+
+// One staged group against the wave's 16 columns: scores, causal mask, online softmax, P.V (and
+// the value policy's corrections when VP > 0).
+template <int D, int R, bool VQ2, bool NB, int VP>
 __device__ __forceinline__ void group_step(const uint8_t* T, const Fixed<D, R>& f, float kappa, int tok0,
                                            bool masked, int n_att, float* lg_row, int n, int quad, int lane,
                                            floatx4* o_acc, float* z_acc, float& m_run, float& l_run) {
-  using TL = Tile<D, R, VQ2, NB>;
+  using TL = Tile<D, R, VQ2, NB, VP>;
   constexpr int NKT = D / 32, NCT = D / 16, NG = D / 32;
   const _Float16* km_h = reinterpret_cast<const _Float16*>(T + TL::OFF_KM);
   const int row_tok0 = 8 * (n / 4) + (n % 4);  // token of this lane's row in tile 0 (tile 1: +4)
@@ -242,6 +271,8 @@ __device__ __forceinline__ void group_step(const uint8_t* T, const Fixed<D, R>& 
       o_acc[2 * cg + 1] = mfma_bf16(a1, bh, o_acc[2 * cg + 1]);
       o_acc[2 * cg + 1] = mfma_bf16(a1, bl, o_acc[2 * cg + 1]);
     }
+    if constexpr (VP > 0)
+      add_corrections<D, VP>(T + TL::OFF_VP, *reinterpret_cast<const uint32_t*>(T + TL::OFF_VI), p, n, quad, o_acc);
   } else {
     bf16x8_t p_hi, p_lo;
 #pragma unroll
@@ -360,12 +391,13 @@ __device__ __forceinline__ void tail_step(const PrefillArgs& a, int64_t bh, int6
   }
 }
 
-template <int D, int R, bool VQ2, bool NB>
+template <int D, int R, bool VQ2, bool NB, int VP>
 __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
-  using TL = Tile<D, R, VQ2, NB>;
+  static_assert(VP == 0 || (VQ2 && !NB), "the value policy is built for 2-bit values and 2-bit keys");
+  using TL = Tile<D, R, VQ2, NB, VP>;
   constexpr int RU = R > 0 ? R : 1;
   constexpr int NKT = D / 32, NCT = D / 16, NG = D / 32;
-  using ST = Stage<D, R, VQ2, NB>;
+  using ST = Stage<D, R, VQ2, NB, VP>;
   __shared__ u32x4 tile_s[2][TL::CHUNKS];
   __shared__ float qs[kCols][D];        // scaled queries of the workgroup's columns
   __shared__ float qu_s[kCols][RU];     // U^T q (scaled)
@@ -471,6 +503,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
   // to arrive before it is staged
   constexpr int PD = 3;
   u32x4 pf[PD][ST::KV];
+  uint32_t pidx[PD];  // VP > 0: each group's index word (one uniform load)
   // the arrays of this stream: byte base and size of the region the group offsets index
   const int64_t groups_cap = a.cap / kGroup;
   auto arr_base = [&](int i) -> const char* {  // i is a compile-time constant at every use
@@ -480,7 +513,8 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
       case 2: return (const char*)a.scode;
       case 3: return (const char*)a.ssc;
       case 4: return (const char*)a.vmeta;
-      default: return VQ2 ? (const char*)a.vcode : (const char*)a.vdense;
+      case 5: return VQ2 ? (const char*)a.vcode : (const char*)a.vdense;
+      default: return (const char*)a.vprot;
     }
   };
   // piece 4 * j + wave of a group: its array A (wave-uniform, by scalar compares) and chunk
@@ -490,7 +524,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
     for (int i = 1; i < ST::NARR; ++i) A = (ST::pieces(i) > 0 && q >= ST::first(i)) ? i : A;
     return A;
   };
-  auto fetch_into = [&](u32x4* dst, int64_t gi) {
+  auto fetch_into = [&](u32x4* dst, uint32_t& idx, int64_t gi) {
     // contiguous caches: one resource per stream and array, the group by offset; paged caches:
     // the group's block (page * Hkv + h) as its own resource
     const bool paged = a.map.block_table != nullptr;
@@ -513,8 +547,12 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
       // the group and is not staged), so each step issues the same loads and its waits count exactly
       dst[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * (64 * (q - first) + lane), soff, 0);
     }
+    if constexpr (VP > 0) {
+      const __amdgpu_buffer_rsrc_t ri = stage_rsrc(a.vpidx + blk, paged ? 4 : groups_cap * 4);
+      idx = __builtin_amdgcn_raw_buffer_load_b32(ri, 0, __builtin_amdgcn_readfirstlane(paged ? 0 : (int)(gi * 4)), 0);
+    }
   };
-  auto stage_from = [&](const u32x4* src, int buf) {
+  auto stage_from = [&](const u32x4* src, uint32_t idx, int buf) {
 #pragma unroll
     for (int j = 0; j < ST::KV; ++j) {
       const int q = 4 * j + wave, A = piece_array(q);
@@ -529,14 +567,16 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
       const int chunk = 64 * (q - first) + lane;
       if (q < ST::first(ST::NARR) && chunk < chunks) tile_s[buf][off / 16 + chunk] = src[j];
     }
+    if constexpr (VP > 0)
+      if (tid == 0) reinterpret_cast<uint32_t*>(tile_s[buf])[TL::OFF_VI / 4] = idx;
   };
   // Requests are unconditional (indices past the last group read the last group again, unused),
   // so every step issues the same loads in the same order and each wait counts exactly.
   auto clamp_g = [&](int64_t x) { return x < G ? x : G - 1; };
   if (G > 0) {
 #pragma unroll
-    for (int k = 0; k < PD; ++k) fetch_into(pf[k], clamp_g(k));
-    stage_from(pf[0], 0);
+    for (int k = 0; k < PD; ++k) fetch_into(pf[k], pidx[k], clamp_g(k));
+    stage_from(pf[0], pidx[0], 0);
   }
   __syncthreads();
   for (int64_t g0 = 0; g0 < G; g0 += PD) {
@@ -544,13 +584,13 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
     for (int k = 0; k < PD; ++k) {
       const int64_t gi = g0 + k;
       if (gi >= G) break;
-      fetch_into(pf[k], clamp_g(gi + PD));  // set k held group gi, staged in the step before
+      fetch_into(pf[k], pidx[k], clamp_g(gi + PD));  // set k held group gi, staged in the step before
       const int64_t tok0 = gi * kGroup;
       if (tok0 < att_max_w)
-        group_step<D, R, VQ2, NB>(reinterpret_cast<const uint8_t*>(tile_s[gi & 1]), f, a.corr_scale, (int)tok0,
+        group_step<D, R, VQ2, NB, VP>(reinterpret_cast<const uint8_t*>(tile_s[gi & 1]), f, a.corr_scale, (int)tok0,
                                   tok0 + kGroup > att_min_w, (int)n_att, lg_row, n, quad, lane, o_acc, z_acc, m_run,
                                   l_run);
-      stage_from(pf[(k + 1) % PD], (int)((gi + 1) & 1));  // group gi + 1 (past the end: unused)
+      stage_from(pf[(k + 1) % PD], pidx[(k + 1) % PD], (int)((gi + 1) & 1));  // group gi + 1 (past the end: unused)
       __syncthreads();
     }
   }
@@ -592,19 +632,29 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
   }
 }
 
-template <int D, bool VQ2, bool NB>
-hipError_t launch_r(const PrefillArgs& a, hipStream_t s) {
+template <int D, bool VQ2, bool NB, int VP>
+hipError_t launch_rp(const PrefillArgs& a, hipStream_t s) {
   const int64_t n_cols = a.n_q * a.gqa;
   dim3 grid((unsigned)((n_cols + kCols - 1) / kCols), (unsigned)a.hkv, (unsigned)a.batch);
   switch (a.r) {
-    case 0: hipLaunchKernelGGL((prefill_mfma_kernel<D, 0, VQ2, NB>), grid, dim3(kThreads), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((prefill_mfma_kernel<D, 4, VQ2, NB>), grid, dim3(kThreads), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((prefill_mfma_kernel<D, 8, VQ2, NB>), grid, dim3(kThreads), 0, s, a); break;
-    case 16: hipLaunchKernelGGL((prefill_mfma_kernel<D, 16, VQ2, NB>), grid, dim3(kThreads), 0, s, a); break;
-    case 32: hipLaunchKernelGGL((prefill_mfma_kernel<D, 32, VQ2, NB>), grid, dim3(kThreads), 0, s, a); break;
+    case 0: hipLaunchKernelGGL((prefill_mfma_kernel<D, 0, VQ2, NB, VP>), grid, dim3(kThreads), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((prefill_mfma_kernel<D, 4, VQ2, NB, VP>), grid, dim3(kThreads), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((prefill_mfma_kernel<D, 8, VQ2, NB, VP>), grid, dim3(kThreads), 0, s, a); break;
+    case 16: hipLaunchKernelGGL((prefill_mfma_kernel<D, 16, VQ2, NB, VP>), grid, dim3(kThreads), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((prefill_mfma_kernel<D, 32, VQ2, NB, VP>), grid, dim3(kThreads), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <int D, bool VQ2, bool NB>
+hipError_t launch_r(const PrefillArgs& a, hipStream_t s) {
+  if constexpr (VQ2 && !NB) {
+    if (a.value_protect == 1) return launch_rp<D, true, false, 1>(a, s);
+    if (a.value_protect == 2) return launch_rp<D, true, false, 2>(a, s);
+  }
+  if (a.value_protect) return hipErrorInvalidValue;
+  return launch_rp<D, VQ2, NB, 0>(a, s);
 }
 
 }  // namespace

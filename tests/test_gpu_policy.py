@@ -5,8 +5,8 @@ bit for bit (a discrete decision both sides take in the same f32/f64 arithmetic)
 which adds p_t * correction_t for the chosen tokens, must meet the decode tolerances against the
 oracle's fp64 decode of its own cache. Cases: one and two corrected tokens, d = 64 and 128, one
 group per matrix product (g = 16) and two groups sharing the columns (g <= 8), dense tails, splits,
-the two-groups-per-workgroup append of long writes, paged caches; the score-space diagnostics
-(A^2 with the corrections); the chunked prefill rejects such caches.
+the two-groups-per-workgroup append of long writes, paged caches; the chunked prefill and the
+score-space diagnostics (A^2 with the corrections).
 """
 import numpy as np
 import pytest
@@ -93,15 +93,37 @@ def test_paged_ragged_rows():
     _run(w, 3, 160, (40, 1, 30, 33, 2), out_bf16=True, value_protect=2, a_dir=_direction(w))
 
 
-def test_prefill_rejects_policy_caches():
+@pytest.mark.parametrize("P", [1, 2])
+def test_chunked_prefill_with_corrections(P):
+    """The chunked prefill reads the corrections as the decode does: logits and outputs of sampled
+    query tokens against the oracle's prefill over its own policy cache."""
     import torch
-    import quantized_kv_cache_headq_amd as hq
     w = synth.scaled(W["qwen14b_fullkv"], n_q_heads=10, n_kv_heads=2)
-    U = orc.calibrate(synth.calibration_queries(w, n_cal=64), w.n_kv_heads, w.rank)[0]
-    dc, K, V = gpu_cache(w, U, 1, 64, 64, value_protect=1, a_dir=_direction(w))
-    q = torch.zeros((1, 4, w.n_q_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
-    with pytest.raises(hq.HeadQError, match="UNSUPPORTED"):
-        dc.prefill(q, 60)
+    B, start, n_q, cap = 2, 70, 40, 128
+    L = start + n_q
+    say("policy-prefill", w.name, f"P={P} B={B} start={start} n_q={n_q}")
+    U = orc.calibrate(synth.calibration_queries(w, n_cal=128), w.n_kv_heads, w.rank)[0]
+    a = _direction(w)
+    pieces = [(0, 64), (64, 6), (70, 40)]
+    dc, K, V = gpu_cache(w, U, B, L, cap, pieces=pieces, value_protect=P, a_dir=a)
+    oc = orc.empty_cache(B, w.n_kv_heads, cap, w.head_dim, w.rank, 1, VDT[w.value_dtype],
+                         key_dtype=VDT[w.key_dtype], value_protect=P)
+    for b in range(B):
+        for h in range(w.n_kv_heads):
+            for st, n in pieces:
+                orc.write_stream(oc, b, h, st, K[b, h, st:st + n], value_payload(V[b, h, st:st + n], w), U[h], 1,
+                                 VDT[w.value_dtype], a_h=a[h])
+    compare_cache(dc, oc)
+    q = synth.decode_queries(w, batch=B * n_q, stream=5).reshape(B, n_q, w.n_q_heads, w.head_dim)
+    lg = torch.full((B, n_q, w.n_q_heads, L), float("nan"), device="cuda")
+    out = dc.prefill(to_device(q, w.query_dtype), start, logits_dbg=lg)
+    torch.cuda.synchronize()
+    lg, out = lg.cpu().numpy(), out.float().cpu().numpy()
+    tokens = [0, 7, 25, 39]
+    ref_l, ref_o = orc.prefill(oc, q, U, start, 1.0, 1, VDT[w.value_dtype], tokens=tokens)
+    for t in tokens:
+        check_logits(lg[:, t, :, :start + t + 1], ref_l[:, t, :, :start + t + 1])
+        check_out(out[:, t], ref_o[:, t], False)
 
 
 @pytest.mark.parametrize("P", [0, 2])
