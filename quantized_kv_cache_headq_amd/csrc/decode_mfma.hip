@@ -1,4 +1,4 @@
-// decode_mfma.hip — headq_decode_attn on gfx950 matrix cores (dense bf16 values).
+// decode_mfma.hip — headq_decode_attn on gfx950 matrix cores (dense bf16 or 2-bit values).
 //
 // HeadQ technical summary ("Technische Samenvatting"), §3 step 3 (Cache Uitlezen): the runtime
 // query decodes the side code through U_h^T q, the logit is corrected additively,
@@ -37,6 +37,8 @@
 // Splits of a stream are merged in the same launch: each workgroup publishes its partial,
 // fences, and counts itself in on the stream's workspace counter; the last one merges by
 // log-sum-exp, writes the output and zeroes the counter again.
+// With 2-bit values and g <= 8, J groups share the 16 columns (process_block); with the A^2
+// value policy, each group's corrections are staged with it and added after the P.V product.
 #include <hip/hip_runtime.h>
 
 #include "headq_internal.h"

@@ -9,9 +9,9 @@
 //
 // With many query tokens the cache reads are shared. A workgroup owns 64 (query token, head)
 // columns of one (b, h) stream, 16 per wave, and walks the stream's 32-token groups once: the
-// whole workgroup stages each group in LDS with 16-byte loads (double-buffered: the next group's
-// loads are in flight while the current one is computed) and every wave contracts it against its
-// 16 columns on the matrix cores, as the decode does with its 16 heads:
+// whole workgroup stages each group in LDS with 16-byte loads (two LDS buffers; the next three
+// groups' loads are in flight in registers while a group is computed) and every wave contracts it
+// against its 16 columns on the matrix cores, as the decode does with its 16 heads:
 //   scores^T [32 tok x 16 cols] = codes . (q o s)^T  (+ q.z)  + zc . (U^T q)^T scaled by sigma_j
 //   out^T    [d x 16 cols]     += V^T . P^T
 // with the decode's operand precision (the f32 factors split into high and low half-precision
@@ -37,7 +37,8 @@ constexpr float kLazyMax = 8.0f;          // rescale only when the max grows by 
 // Bytes of one 32-token group as staged in LDS (each array of a group is one contiguous block of
 // the cache): packed key codes 32 x d/4 | key step/zero rows 2 x d x 2 | side codes 32 x r/2 |
 // sigma 32 x 2 | (2-bit values) value step/zero rows 2 x d/32 x 32 x 2 | values (dense bf16
-// [d][32], or 2-bit codes d x 8 in matrix-operand order).
+// [d][32], or 2-bit codes d x 8 in matrix-operand order) | (A^2 value policy) corrections
+// [P][d] bf16 | their token-index word, padded to 16 bytes.
 template <int D, int R, bool VQ2, bool NB, int VP = 0>
 struct Tile {
   static constexpr int KC = kGroup * D / (NB ? 2 : 4), KM = 4 * D, SC = kGroup * R / 2, SG = R > 0 ? kGroup * 2 : 0;
