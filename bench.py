@@ -21,6 +21,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -408,6 +409,62 @@ def run_diagnostics(args, hq, synth, torch, np):
     print(json.dumps(result), flush=True)
 
 
+def time_graphs(torch, np, run, stream, n_caches, n_layers, args, tok_heads, eager_ms):
+    """The step (every layer's append and decode) captured once per cache rotation in a HIP graph
+    and replayed: the eager step time minus the replayed one is the host launch overhead. The
+    library's calls are plain kernel launches on the given stream (no allocation, copy or memset),
+    so they capture as they are."""
+    period = n_caches // math.gcd(n_caches, n_layers)
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        for i in range(period):
+            run(i, stream=side)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for i in range(period):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run(i, stream=torch.cuda.current_stream())
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for i in range(args.warmup):
+        graphs[i % period].replay()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        graphs[i % period].replay()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    return {"ms_per_step": ms, "value": tok_heads / (ms / 1e3), "graphs": period,
+            "launch_overhead_us_per_layer": (eager_ms - ms) * 1e3 / n_layers}
+
+
+def split_sweep(torch, np, hq, cfg, caches, q, out, n_ctx, stream, args):
+    """Decode alone (no append) at each requested split count, caches rotated as in the step."""
+    res = {}
+    for S in [int(x) for x in args.split_sweep.split(",") if x.strip()]:
+        nb = hq.decode_workspace_bytes(cfg, n_ctx, S)
+        ws = torch.zeros((nb + 3) // 4, dtype=torch.float32, device=q.device)
+        for i in range(args.warmup):
+            caches[i % len(caches)].decode(q, n_ctx, out=out, out_dtype=hq.HEADQ_BF16, n_splits=S, ws=ws,
+                                           stream=stream)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            ev[i][0].record(stream)
+            caches[i % len(caches)].decode(q, n_ctx, out=out, out_dtype=hq.HEADQ_BF16, n_splits=S, ws=ws,
+                                           stream=stream)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        res[str(S) if S else "auto"] = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -423,6 +480,10 @@ def main():
     ap.add_argument("--copy-probe", action="store_true", help="launch one 1 GiB device copy (counter scaling)")
     ap.add_argument("--value-protect", type=int, default=0,
                     help="A^2 value policy: corrected tokens per 32-token group (2-bit value workloads)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured in HIP graphs (one per cache rotation) and replayed")
+    ap.add_argument("--split-sweep", default="",
+                    help="comma-separated split counts: also time the decode alone at each (0 = library choice)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -509,7 +570,7 @@ def main():
     # One step: decode workloads append the newest 32-token group of every stream and decode over
     # the whole context, once per layer (each layer its own cache); the prefill workload appends
     # the whole prefill.
-    def run(i, marks=None):
+    def run(i, marks=None, stream=stream):
         if append_only:
             dc = caches[i % len(caches)]
             if marks:
@@ -632,6 +693,10 @@ def main():
             "append_ms": float(append_ms.mean()),
             "kv_head_tokens_per_s": w.batch * w.n_kv_heads * n_ctx * n_layers / (ms_per_step / 1e3),
         })
+    if args.graph and not append_only:
+        result["graph"] = time_graphs(torch, np, run, stream, len(caches), n_layers, args, tok_heads, ms_per_step)
+    if args.split_sweep and not append_only:
+        result["split_sweep_decode_ms"] = split_sweep(torch, np, hq, cfg, caches, q, out, n_ctx, stream, args)
     result["calibrate_s_host"] = calib_s
     result["wall_s_timed"] = wall
     if not args.no_cpu_baseline and not append_only:
