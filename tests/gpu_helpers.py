@@ -9,7 +9,7 @@ import numpy as np
 from oracle import oracle as orc
 from workloads import synth
 
-from .helpers import VDT, VMODE, oracle_cache
+from .helpers import VDT, VMODE, oracle_cache, value_payload
 
 DT = {"f32": 0, "bf16": 1}
 
@@ -120,6 +120,21 @@ def oracle_for(w, U, K, V, cap):
     B, H, T, _ = K.shape
     kv = {(b, h): (K[b, h], V[b, h]) for b in range(B) for h in range(H)}
     oc, _ = oracle_cache(w, U, batch=B, n_tok=T, cap=cap, kv=kv)
+    return oc
+
+
+def oracle_pieces(w, U, K, V, cap, pieces):
+    """The oracle's cache of the same generator (or hand-built) arrays, written in the same pieces
+    [(start, n), ...] as the GPU cache (tokens past the last whole group go to the tails)."""
+    B, H = K.shape[:2]
+    oc = orc.empty_cache(B, H, cap, w.head_dim, 0 if U is None else U.shape[2], VMODE[w.value_mode],
+                         VDT[w.value_dtype], key_dtype=VDT[w.key_dtype], base_bits=w.base_bits)
+    for b in range(B):
+        for h in range(H):
+            for st, n in pieces:
+                orc.write_stream(oc, b, h, st, K[b, h, st:st + n], value_payload(V[b, h, st:st + n], w),
+                                 None if U is None else U[h], VMODE[w.value_mode], VDT[w.value_dtype],
+                                 bits=w.base_bits)
     return oc
 
 

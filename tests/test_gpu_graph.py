@@ -12,25 +12,11 @@ import pytest
 from oracle import oracle as orc
 from workloads import synth
 
-from .gpu_helpers import check_out, compare_cache, gpu_cache, say, to_device
-from .helpers import VDT, VMODE, value_payload
+from .gpu_helpers import check_out, compare_cache, gpu_cache, oracle_pieces, say, to_device
 
 pytestmark = pytest.mark.gpu
 
 W = synth.WORKLOADS
-
-
-def _oracle(w, U, K, V, cap, pieces):
-    """The oracle's cache of the same generator arrays, written in the same pieces."""
-    B, H = K.shape[:2]
-    oc = orc.empty_cache(B, H, cap, w.head_dim, U.shape[2], VMODE[w.value_mode], VDT[w.value_dtype],
-                         key_dtype=VDT[w.key_dtype], base_bits=w.base_bits)
-    for b in range(B):
-        for h in range(H):
-            for st, n in pieces:
-                orc.write_stream(oc, b, h, st, K[b, h, st:st + n], value_payload(V[b, h, st:st + n], w), U[h],
-                                 VMODE[w.value_mode], VDT[w.value_dtype], bits=w.base_bits)
-    return oc
 
 
 @pytest.mark.parametrize("wname,B,T,new,n_splits,bf16", [
@@ -66,7 +52,7 @@ def test_captured_step_replays_equal_eager(wname, B, T, new, n_splits, bf16):
 
     step(torch.cuda.current_stream(), out_e)
     torch.cuda.synchronize()
-    oc = _oracle(w, U, K, V, cap, pieces)
+    oc = oracle_pieces(w, U, K, V, cap, pieces)
     _, ref = orc.decode(oc, q, U, T, 1.0, 0 if w.value_mode == "dense" else 1, 0 if w.value_dtype == "f32" else 1)
     check_out(out_e.float().cpu().numpy(), ref, bf16)
 
