@@ -23,6 +23,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -94,7 +95,15 @@ def copy_probe(torch, dev):
 
 
 def source_sha(src: str) -> str:
-    return hashlib.sha256(open(os.path.join(CSRC, src), "rb").read()).hexdigest()[:16]
+    """Hash of a kernel's source file and of the library's own headers it includes."""
+    h = hashlib.sha256()
+    text = open(os.path.join(CSRC, src), "rb").read()
+    h.update(text)
+    for inc in re.findall(rb'^#include "([^"]+)"', text, flags=re.M):
+        path = os.path.join(CSRC, inc.decode())
+        if os.path.exists(path):
+            h.update(open(path, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def traffic_per_launch(workload: str):

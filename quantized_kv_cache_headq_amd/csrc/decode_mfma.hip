@@ -263,7 +263,6 @@ struct Fixed {
   half4_t bu_hi4, bu_lo4;          // U^T q at ranks 4*quad + j (16x16x16 path)
   half8_t bu_hi8, bu_lo8;          // U^T q at ranks 8*quad + j (16x16x32 path, r = 32)
   float inv_scale;                 // 2^e: undoes the per-head query scale
-  float kappa;                     // corr_scale
 };
 
 // Stage the lane's raw bytes of one group into a wave's LDS slot (the caller orders the slot's
@@ -378,8 +377,9 @@ __device__ __forceinline__ void group_logits(const uint8_t* slot, const Fixed<D,
   }
 }
 
-// Scores (log2 units) of tokens 8*quad + j for this lane's column: the corrected logit
-// inv_scale * (acc + kappa * sigma_j * cr), sigma from the group staged in `slot`.
+// Scores of tokens 8*quad + j for this lane's column before the head's power-of-two scale (log2
+// units once scaled): acc + sigma_j * cr, sigma from the group staged in `slot` (the correction
+// scale kappa is folded into U^T q).
 template <int D, int R, bool VQ2, bool NB>
 __device__ __forceinline__ void group_scores(const uint8_t* slot, const Fixed<D, R>& f, int quad, const floatx4* acc,
                                              const floatx4* cr, float* sv) {
@@ -390,25 +390,26 @@ __device__ __forceinline__ void group_scores(const uint8_t* slot, const Fixed<D,
     for (int T = 0; T < 2; ++T)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        sv[4 * T + j] = f.inv_scale * fmaf(f.kappa * (float)sg[4 * T + j], cr[T][j], acc[T][j]);
+        sv[4 * T + j] = fmaf((float)sg[4 * T + j], cr[T][j], acc[T][j]);
   } else {
 #pragma unroll
     for (int T = 0; T < 2; ++T)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) sv[4 * T + j] = f.inv_scale * acc[T][j];
+      for (int j = 0; j < 4; ++j) sv[4 * T + j] = acc[T][j];
   }
 }
 
-// Online-softmax step (lazy maximum) over this lane's 8 scores; p = 2^(s - m_run), with live =
-// false giving p = 0 and no update (a column whose group does not exist in this step).
+// Online-softmax step (lazy maximum) over this lane's 8 scores s = inv_scale * sv; p = 2^(s - m_run),
+// with live = false giving p = 0 and no update (a column whose group does not exist in this step).
+// inv_scale is a power of two, so scaling the maximum, or each score inside the exponent's fma,
+// rounds exactly as scaling the scores first would.
 template <int NCT, int NG, bool VQ2>
-__device__ __forceinline__ void softmax_step(const float* sv, bool live, float* p, floatx4* o_acc, float* z_acc,
-                                             float& m_run, float& l_run) {
+__device__ __forceinline__ void softmax_step(const float* sv, float inv_scale, bool live, float* p, floatx4* o_acc,
+                                             float* z_acc, float& m_run, float& l_run) {
   float mx = sv[0];
 #pragma unroll
   for (int j = 1; j < 8; ++j) mx = fmaxf(mx, sv[j]);
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  mx = inv_scale * quad_max(mx);
   const bool grow = live && mx > m_run + kLazyMax;  // true on the first group (m_run = -inf)
   if (__any(grow)) {
     // alpha: 0 on a column's first group; exactly 1 for the columns that keep their maximum
@@ -425,7 +426,7 @@ __device__ __forceinline__ void softmax_step(const float* sv, bool live, float* 
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    p[j] = live ? __builtin_amdgcn_exp2f(sv[j] - m_run) : 0.0f;  // v_exp_f32; below 2^-126 flushes to 0
+    p[j] = live ? __builtin_amdgcn_exp2f(fmaf(inv_scale, sv[j], -m_run)) : 0.0f;  // below 2^-126 flushes to 0
     l_run += p[j];
   }
 }
@@ -482,10 +483,10 @@ __device__ __forceinline__ void process_group(const GroupRaw<D, R, VQ2, NB>& cur
   if (a.logits_dbg && n < g) {
     float* dst = a.logits_dbg + ((int64_t)b * a.hq + hq0 + n) * a.n_ctx + (int64_t)gi * kGroup + 8 * quad;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) dst[j] = sv[j] * kLn2;
+    for (int j = 0; j < 8; ++j) dst[j] = f.inv_scale * sv[j] * kLn2;
   }
   float p[8];
-  softmax_step<NCT, NG, VQ2>(sv, true, p, o_acc, z_acc, m_run, l_run);
+  softmax_step<NCT, NG, VQ2>(sv, f.inv_scale, true, p, o_acc, z_acc, m_run, l_run);
   if constexpr (VQ2) {
     bf16x8_t bh[NG], bl[NG];
     value_operands<D, R, NB>(slot, p, quad, bh, bl, z_acc);
@@ -561,10 +562,10 @@ __device__ __forceinline__ void process_block(const typename Bytes<D / 8>::T* vc
     for (int j = 1; j < J; ++j) gi = jl == j ? gis[j] : gi;
     float* dst = a.logits_dbg + ((int64_t)b * a.hq + hq0 + hd) * a.n_ctx + (int64_t)gi * kGroup + 8 * quad;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) dst[j] = sv[j] * kLn2;
+    for (int j = 0; j < 8; ++j) dst[j] = f.inv_scale * sv[j] * kLn2;
   }
   float p[8];
-  softmax_step<NCT, NG, true>(sv, live, p, o_acc, z_acc, m_run, l_run);
+  softmax_step<NCT, NG, true>(sv, f.inv_scale, live, p, o_acc, z_acc, m_run, l_run);
   bf16x8_t bh[NG], bl[NG];
   value_operands<D, R, NB>(own, p, quad, bh, bl, z_acc);
   const bf16x8_t zero8 = bitcast<bf16x8_t>((u32x4){0u, 0u, 0u, 0u});
@@ -653,8 +654,7 @@ __device__ __forceinline__ void process_tail(const DecodeArgs& a, int64_t n_ctx,
   float mx = sv[0];
 #pragma unroll
   for (int j = 1; j < 8; ++j) mx = fmaxf(mx, sv[j]);
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  mx = quad_max(mx);
   const bool grow = mx > m_run + kLazyMax;
   if (__any(grow)) {
     const float m_new = grow ? mx : m_run;
@@ -848,7 +848,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       float acc = 0.0f;
       if (hh < g)
         for (int c = 0; c < D; ++c) acc = fmaf(U_s[c * R + r], qs[hh][c], acc);
-      qu_s[hh][r] = acc;
+      qu_s[hh][r] = a.corr_scale * acc;  // the correction's scale rides on U^T q
     }
   }
   __syncthreads();
@@ -864,7 +864,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       f.bq_lo[t][j] = f16_lo(x);
     }
   f.inv_scale = inv_scale_s[hd];
-  f.kappa = a.corr_scale;
   if constexpr (R == 32) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -959,16 +958,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
     for (int cg = 0; cg < NG; ++cg) {
       float z = z_acc[cg];
-      z += __shfl_xor(z, 16);
-      z += __shfl_xor(z, 32);
+      z = quad_sum(z);
       o_acc[2 * cg] += z;
       o_acc[2 * cg + 1] += z;
     }
   }
 
   // ---- merge the 4 waves of this workgroup, write the split partial
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
+  l_run = quad_sum(l_run);
   if (quad == 0) {
     m_w[wave][n] = m_run;
     l_w[wave][n] = l_run;

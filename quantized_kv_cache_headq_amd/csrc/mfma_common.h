@@ -85,6 +85,25 @@ __device__ __forceinline__ floatx4 mfma_f16k16(const half4_t& a, const half4_t& 
   return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
 
+// Reductions over the four lanes n, n + 16, n + 32, n + 48 of a wave64 (the four token quads of a
+// matrix-product column) in registers: gfx950's lane-row swaps, given one value twice, return at
+// every lane its own value and that of the lane 16 (or 32) apart.
+__device__ __forceinline__ float partner16_op_max(float x) {
+  const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float partner32_op_max(float x) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float quad_max(float x) { return partner32_op_max(partner16_op_max(x)); }
+__device__ __forceinline__ float quad_sum(float x) {
+  const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+  const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
+}
+
 // x ~ hi + lo in bf16 pairs: hi truncated (the upper half of the f32), lo the remainder rounded
 // to nearest; together ~16 significant bits.
 __device__ __forceinline__ void split_bf16_pair(float x0, float x1, uint32_t& hi, uint32_t& lo) {

@@ -119,7 +119,7 @@ __device__ __forceinline__ void add_corrections(const uint8_t* prow, uint32_t id
 // One staged group against the wave's 16 columns: scores, causal mask, online softmax, P.V (and
 // the value policy's corrections when VP > 0).
 template <int D, int R, bool VQ2, bool NB, int VP>
-__device__ __forceinline__ void group_step(const uint8_t* T, const Fixed<D, R>& f, float kappa, int tok0,
+__device__ __forceinline__ void group_step(const uint8_t* T, const Fixed<D, R>& f, int tok0,
                                            bool masked, int n_att, float* lg_row, int n, int quad, int lane,
                                            floatx4* o_acc, float* z_acc, float& m_run, float& l_run) {
   using TL = Tile<D, R, VQ2, NB, VP>;
@@ -167,7 +167,9 @@ __device__ __forceinline__ void group_step(const uint8_t* T, const Fixed<D, R>& 
       acc[Ti] = mfma_f16(ac, p_lo, acc[Ti]);
     }
   }
-  float sv[8];  // scores (log2 units) of tokens 8*quad + j for column n
+  // scores of tokens 8*quad + j for column n, in log2 units before the column's power-of-two
+  // scale (applied in the softmax; the correction scale is folded into U^T q)
+  float sv[8];
   if constexpr (R > 0) {
     floatx4 cr[2];
 #pragma unroll
@@ -193,12 +195,12 @@ __device__ __forceinline__ void group_step(const uint8_t* T, const Fixed<D, R>& 
     for (int Ti = 0; Ti < 2; ++Ti)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        sv[4 * Ti + j] = f.inv_scale * fmaf(kappa * (float)sg[4 * Ti + j], cr[Ti][j], acc[Ti][j]);
+        sv[4 * Ti + j] = fmaf((float)sg[4 * Ti + j], cr[Ti][j], acc[Ti][j]);
   } else {
 #pragma unroll
     for (int Ti = 0; Ti < 2; ++Ti)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) sv[4 * Ti + j] = f.inv_scale * acc[Ti][j];
+      for (int j = 0; j < 4; ++j) sv[4 * Ti + j] = acc[Ti][j];
   }
   if (masked) {
 #pragma unroll
@@ -208,15 +210,15 @@ __device__ __forceinline__ void group_step(const uint8_t* T, const Fixed<D, R>& 
   if (lg_row) {
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      if (tok0 + 8 * quad + j < n_att) lg_row[tok0 + 8 * quad + j] = sv[j] * kLn2;
+      if (tok0 + 8 * quad + j < n_att) lg_row[tok0 + 8 * quad + j] = f.inv_scale * sv[j] * kLn2;
   }
 
-  // online softmax (lazy maximum); masked tokens weigh 0
+  // online softmax (lazy maximum); masked tokens weigh 0. The scale is a power of two, so scaling
+  // the maximum, or each score inside the exponent's fma, rounds exactly as scaling first would.
   float mx = sv[0];
 #pragma unroll
   for (int j = 1; j < 8; ++j) mx = fmaxf(mx, sv[j]);
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  mx = f.inv_scale * quad_max(mx);
   const bool grow = mx > m_run + kLazyMax;  // true on a column's first unmasked group
   if (__any(grow)) {
     const float m_new = grow ? mx : m_run;
@@ -232,10 +234,11 @@ __device__ __forceinline__ void group_step(const uint8_t* T, const Fixed<D, R>& 
   float p[8];
   if (masked) {  // a column whose limit falls in this group may see only masked scores (m_run = -inf)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) p[j] = sv[j] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(sv[j] - m_run);
+    for (int j = 0; j < 8; ++j)
+      p[j] = sv[j] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(fmaf(f.inv_scale, sv[j], -m_run));
   } else {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(sv[j] - m_run);
+    for (int j = 0; j < 8; ++j) p[j] = __builtin_amdgcn_exp2f(fmaf(f.inv_scale, sv[j], -m_run));
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) l_run += p[j];
@@ -345,8 +348,7 @@ __device__ __forceinline__ void tail_step(const PrefillArgs& a, int64_t bh, int6
   float mx = sv[0];
 #pragma unroll
   for (int j = 1; j < 8; ++j) mx = fmaxf(mx, sv[j]);
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  mx = quad_max(mx);
   const bool grow = mx > m_run + kLazyMax;
   if (__any(grow)) {
     const float m_new = grow ? mx : m_run;
@@ -393,7 +395,7 @@ __device__ __forceinline__ void tail_step(const PrefillArgs& a, int64_t bh, int6
 }
 
 template <int D, int R, bool VQ2, bool NB, int VP>
-__global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void prefill_mfma_kernel(PrefillArgs a) {
   static_assert(VP == 0 || (VQ2 && !NB), "the value policy is built for 2-bit values and 2-bit keys");
   using TL = Tile<D, R, VQ2, NB, VP>;
   constexpr int RU = R > 0 ? R : 1;
@@ -445,7 +447,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
       const int cl = i / R, r = i % R;
       float acc = 0.0f;
       for (int c = 0; c < D; ++c) acc = fmaf(Uh[c * R + r], qs[cl][c], acc);
-      qu_s[cl][r] = acc;
+      qu_s[cl][r] = a.corr_scale * acc;  // the correction's scale rides on U^T q
     }
   }
   __syncthreads();
@@ -588,7 +590,7 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
       fetch_into(pf[k], pidx[k], clamp_g(gi + PD));  // set k held group gi, staged in the step before
       const int64_t tok0 = gi * kGroup;
       if (tok0 < att_max_w)
-        group_step<D, R, VQ2, NB, VP>(reinterpret_cast<const uint8_t*>(tile_s[gi & 1]), f, a.corr_scale, (int)tok0,
+        group_step<D, R, VQ2, NB, VP>(reinterpret_cast<const uint8_t*>(tile_s[gi & 1]), f, (int)tok0,
                                   tok0 + kGroup > att_min_w, (int)n_att, lg_row, n, quad, lane, o_acc, z_acc, m_run,
                                   l_run);
       stage_from(pf[(k + 1) % PD], pidx[(k + 1) % PD], (int)((gi + 1) & 1));  // group gi + 1 (past the end: unused)
@@ -608,14 +610,12 @@ __global__ __launch_bounds__(kThreads) void prefill_mfma_kernel(PrefillArgs a) {
 #pragma unroll
     for (int cg = 0; cg < NG; ++cg) {
       float z = z_acc[cg];
-      z += __shfl_xor(z, 16);
-      z += __shfl_xor(z, 32);
+      z = quad_sum(z);
       o_acc[2 * cg] += z;
       o_acc[2 * cg + 1] += z;
     }
   }
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
+  l_run = quad_sum(l_run);
   if (col < n_cols) {
     const float inv_l = l_run > 0.0f ? 1.0f / l_run : 0.0f;
     const int64_t orow = (((int64_t)b * a.n_q + col / g) * a.hq + hq0 + col % g) * D;
