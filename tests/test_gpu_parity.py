@@ -79,9 +79,15 @@ def test_rank_variants(rank):
     _case(synth.scaled(W["qwen7b_decode"], n_q_heads=8, n_kv_heads=2, rank=rank), 1, 256)
 
 
-@pytest.mark.parametrize("corr", [0.0, -1.0])
+@pytest.mark.parametrize("corr", [0.0, -1.0, 0.5, 2.5])
 def test_correction_scale_controls(corr):
     _case(synth.scaled(W["qwen7b_decode"], n_q_heads=14, n_kv_heads=2), 1, 256, corr=corr)
+
+
+@pytest.mark.parametrize("corr", [0.0, 0.5])
+def test_correction_scale_packed_columns(corr):
+    """The 2-bit value decode with three groups sharing the matrix columns, at other scales."""
+    _case(synth.scaled(W["qwen14b_fullkv"], n_q_heads=10, n_kv_heads=2), 1, 384 + 32, corr=corr, n_splits=2)
 
 
 def test_append_in_pieces_at_offsets():

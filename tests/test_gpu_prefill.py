@@ -77,8 +77,9 @@ def test_tinyllama_shape_d64():
     _run(synth.scaled(W["tinyllama_decode"], n_q_heads=16, n_kv_heads=2), 2, 33, 50)
 
 
-def test_rank32_wrong_sign_and_rank0():
+def test_rank32_wrong_sign_half_scale_and_rank0():
     _run(synth.scaled(W["qwen7b_decode"], n_q_heads=7, n_kv_heads=1, rank=32), 1, 70, 26, kappa=-1.0)
+    _run(synth.scaled(W["qwen7b_decode"], n_q_heads=7, n_kv_heads=1), 1, 70, 26, kappa=0.5)
     _run(synth.scaled(W["qwen7b_decode"], n_q_heads=7, n_kv_heads=1, rank=0), 1, 70, 26)
 
 
