@@ -131,20 +131,30 @@ __global__ __launch_bounds__(128) void diag_prep_kernel(DiagArgs a) {
 // ---- value pass: dv2[b][h][j] = |v_hat_j - v_j|^2 for the A^2 surrogate. A workgroup takes one
 // 32-token group of one stream. Both tiles are staged in LDS with 16-byte loads in their own layout
 // (reference rows [t][c]; the cache's group block [c][t], 2-bit codes and grid as stored, or the
-// tail rows), values widened to f32 (exact for bf16/f32 and the stored dense values); thread
-// (part, t) then sums d/8 channels of token t, and the 8 partial sums are added in part order.
+// tail rows), bf16 values as their raw bits (half the LDS of widened ones, so twice the groups in
+// flight per CU) and f32 values as they are; thread (part, t) then sums d/8 channels of token t
+// exactly in f64, and the 8 partial sums are added in part order.
+template <bool VBF> struct VTile { using T = float; };
+template <> struct VTile<true> { using T = uint16_t; };
 template <bool VBF>
-__device__ __forceinline__ float widen(const uint32_t* w, int e) {  // element e of a 16-byte chunk
-  if constexpr (VBF) return __uint_as_float((e % 2 ? w[e / 2] >> 16 : w[e / 2] & 0xffffu) << 16);
+__device__ __forceinline__ typename VTile<VBF>::T raw_of(const uint32_t* w, int e) {  // element e of a 16-byte chunk
+  if constexpr (VBF) return (uint16_t)(e % 2 ? w[e / 2] >> 16 : w[e / 2] & 0xffffu);
   else return __uint_as_float(w[e]);
+}
+template <bool VBF>
+__device__ __forceinline__ double wide(typename VTile<VBF>::T x) {
+  if constexpr (VBF) return bf16_bits(x);
+  else return (double)x;
 }
 
 template <int D, bool VBF>
 __global__ __launch_bounds__(kThreads) void diag_value_kernel(DiagArgs a) {
   constexpr int CPT = D / 8;                  // channels per thread
-  constexpr int PR = D + 1, PV = kGroup + 1;  // LDS pitches (floats), bank-conflict free reads
-  __shared__ float ref_s[kGroup][PR];         // reference values [t][c]
-  __shared__ float val_s[D][PV];              // the cache's values [c][t] (dense or tail)
+  using ET = typename VTile<VBF>::T;
+  // LDS pitches (elements): the column reads of ref_s (lane = token) hit 32 distinct banks
+  constexpr int PR = VBF ? D + 2 : D + 1, PV = VBF ? kGroup + 2 : kGroup + 1;
+  __shared__ ET ref_s[kGroup][PR];            // reference values [t][c]
+  __shared__ ET val_s[D][PV];                 // the cache's values [c][t] (dense or tail)
   __shared__ __attribute__((aligned(16))) uint8_t code_s[D * 8];  // 2-bit: the code block as stored
   __shared__ __attribute__((aligned(16))) uint16_t meta_s[2 * D];  // 2-bit: step, zero [2][d/32][32]
   __shared__ __attribute__((aligned(16))) uint16_t prot_s[2 * D];  // the value policy's corrections [P][d]
@@ -161,19 +171,19 @@ __global__ __launch_bounds__(kThreads) void diag_value_kernel(DiagArgs a) {
   // reference rows (and tail rows) [t][c] -> LDS
   for (int i = tid; i < kGroup * chunks_row; i += kThreads) {
     const int t = i / chunks_row, c0 = (i % chunks_row) * epc;
-    float x[8] = {0, 0, 0, 0, 0, 0, 0, 0}, y[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    ET x[8] = {0, 0, 0, 0, 0, 0, 0, 0}, y[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     if (t < n_tok) {
       const char* vr = (const char*)a.v_ref + ((int64_t)b * a.vs_b + (int64_t)h * a.vs_h + (g0 + t) * a.vs_t) * es;
       const uint4 u = *reinterpret_cast<const uint4*>(vr + c0 * es);
       const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-      for (int e = 0; e < epc; ++e) x[e] = widen<VBF>(w, e);
+      for (int e = 0; e < epc; ++e) x[e] = raw_of<VBF>(w, e);
       if (tail) {
         const char* vt = (const char*)a.vtail + (bh * kGroup + t) * D * es;
         const uint4 v = *reinterpret_cast<const uint4*>(vt + c0 * es);
         const uint32_t z[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-        for (int e = 0; e < epc; ++e) y[e] = widen<VBF>(z, e);
+        for (int e = 0; e < epc; ++e) y[e] = raw_of<VBF>(z, e);
       }
     }
 #pragma unroll
@@ -192,7 +202,7 @@ __global__ __launch_bounds__(kThreads) void diag_value_kernel(DiagArgs a) {
         const uint4 u = reinterpret_cast<const uint4*>(vg)[i];
         const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-        for (int e = 0; e < epc; ++e) val_s[c][t0 + e] = widen<VBF>(w, e);
+        for (int e = 0; e < epc; ++e) val_s[c][t0 + e] = raw_of<VBF>(w, e);
       }
     } else {
       for (int i = tid; i < D * 8 / 16; i += kThreads)
@@ -230,9 +240,9 @@ __global__ __launch_bounds__(kThreads) void diag_value_kernel(DiagArgs a) {
              f16_bits(meta_s[(D / 32 + gc) * kGroup + t]);
         if (pslot >= 0) vh += bf16_bits(prot_s[pslot * D + c]);
       } else {
-        vh = (double)val_s[c][t];
+        vh = wide<VBF>(val_s[c][t]);
       }
-      const double dv = vh - (double)ref_s[t][c];
+      const double dv = vh - wide<VBF>(ref_s[t][c]);
       e2 = fma(dv, dv, e2);
     }
   }
