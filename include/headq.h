@@ -23,6 +23,10 @@
  *   Streams    GPU calls enqueue work on `stream` (a hipStream_t; NULL = the null stream) and
  *              return without synchronizing. Set HEADQ_SYNC_DEBUG=1 in the environment to make
  *              each GPU call synchronize and report asynchronous errors.
+ *   Graphs     A GPU call is kernel launches on `stream` only (no allocation, copy, memset or
+ *              synchronization outside debug mode), so callers may capture it in a HIP graph;
+ *              the decode workspace's counters return to zero within every call, so a captured
+ *              decode replays with the same workspace.
  *   Errors     Every argument is checked on the host before any HIP call, so a rejected call
  *              enqueues nothing. HEADQ_ERR_HIP reports a launch (or, in debug mode, execution)
  *              error from the HIP runtime.
