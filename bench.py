@@ -160,9 +160,18 @@ def cpu_baseline(w, U, threads: int, rows: int, cpu_seconds: float = 15.0, value
             wall += time.perf_counter() - t0
             passes += 1
     n = passes * rows * w.n_q_heads * w.n_ctx
+    # the same oracle on one thread: whole batch rows in turn for about 2 s
+    rows1, wall1 = 0, 0.0
+    while rows1 == 0 or (wall1 < 2.0 and rows1 < rows):
+        t0 = time.perf_counter()
+        one(rows1)
+        wall1 += time.perf_counter() - t0
+        rows1 += 1
     return {"value": n / wall, "unit": "query-head cached tokens/s", "cores": min(threads, rows), "kind": "oracle",
             "sample": f"fp64 oracle decode of {rows} of {w.batch} batch rows x {w.n_q_heads} query heads x "
-                      f"{w.n_ctx} tokens, {passes} passes ({wall:.2f} s wall, {cpu:.1f} s CPU)"}
+                      f"{w.n_ctx} tokens, {passes} passes ({wall:.2f} s wall, {cpu:.1f} s CPU)",
+            "value_one_thread": rows1 * w.n_q_heads * w.n_ctx / wall1,
+            "sample_one_thread": f"{rows1} batch rows in turn on one thread ({wall1:.2f} s)"}
 
 
 def append_cpu_baseline(w, U, threads: int, cpu_seconds: float = 15.0):
