@@ -534,7 +534,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py: this build runs on exactly one GPU (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "multi-GPU sharding is described in DESIGN.md but not built.", file=sys.stderr)
+              "sharding over several GPUs is not built (the decode would shard over batch rows and KV heads "
+              "with no exchange, each GPU running this kernel on its share).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
