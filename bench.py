@@ -533,7 +533,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build runs on exactly one GPU (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+        print(f"bench.py: the benchmark runs on exactly one GPU (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
               "sharding over several GPUs is not built (the decode would shard over batch rows and KV heads "
               "with no exchange, each GPU running this kernel on its share).", file=sys.stderr)
         sys.exit(2)

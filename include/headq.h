@@ -91,7 +91,7 @@ typedef enum headq_status {
   HEADQ_ERR_CAPACITY = 4,    /* start + n_new > capacity, or n_ctx > capacity */
   HEADQ_ERR_WORKSPACE = 5,   /* *ws_bytes smaller than the size this call needs */
   HEADQ_ERR_NUMERIC = 6,     /* non-finite calibration input */
-  HEADQ_ERR_UNSUPPORTED = 7, /* a well-formed setting this build does not implement */
+  HEADQ_ERR_UNSUPPORTED = 7, /* a well-formed setting libheadq does not implement */
   HEADQ_ERR_HIP = 8          /* the HIP runtime reported an error */
 } headq_status;
 

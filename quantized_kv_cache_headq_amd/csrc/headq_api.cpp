@@ -88,7 +88,7 @@ extern "C" const char* headq_status_string(headq_status s) {
     case HEADQ_ERR_CAPACITY: return "token range exceeds the cache capacity";
     case HEADQ_ERR_WORKSPACE: return "workspace too small";
     case HEADQ_ERR_NUMERIC: return "non-finite input";
-    case HEADQ_ERR_UNSUPPORTED: return "setting not supported by this build";
+    case HEADQ_ERR_UNSUPPORTED: return "setting not supported by libheadq";
     case HEADQ_ERR_HIP: return "HIP runtime error";
   }
   return "unknown status";
