@@ -5,6 +5,7 @@ Argument checks run before any HIP call, so every rejected call here touches no 
 import ctypes
 import re
 import subprocess
+import sys
 
 import numpy as np
 import pytest
@@ -288,3 +289,19 @@ def test_value_policy_settings_are_validated():
     st = lib.headq_cache_append(ctypes.byref(cfg.c()), ctypes.byref(cache), 16, (ctypes.c_int64 * 3)(1, 1, 128),
                                 None, None, 0, 32, None, None)
     assert bd.STATUS[st] == "HEADQ_ERR_NULL"
+
+
+def test_missing_library_fails_loudly():
+    """Without the built library every call raises: there is no CPU or torch fallback."""
+    code = ("import pathlib, numpy as np\n"
+            "import quantized_kv_cache_headq_amd as hq\n"
+            "import quantized_kv_cache_headq_amd.binding as bd\n"
+            "bd.LIB_PATH = pathlib.Path('/nonexistent/libheadq.so')\n"
+            "cfg = hq.Config(128, 28, 4, 1, 64, 16)\n"
+            "try:\n"
+            "    hq.headq_calibrate(cfg, np.zeros((28, 8, 128), np.float32))\n"
+            "except RuntimeError as e:\n"
+            "    print('raised:', e)\n")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.startswith("raised:") and "is missing" in r.stdout
